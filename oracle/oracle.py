@@ -1,0 +1,191 @@
+"""ctypes wrapper of the CPU oracle (pa_oracle.c).
+
+TEST INFRASTRUCTURE: only the test-suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  It shares nothing with the GPU
+library; both sides meet only at the seeded inputs.
+
+All arrays are host numpy arrays in the storage formats of the inputs
+(bf16 as uint16 bits, int8 codes, fp8 e4m3fn codes as uint8).  Pools are
+[num_blocks, block_size, num_kv_heads, head_dim]; int8 scale pools are
+[num_blocks, block_size, num_kv_heads].
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBS = {}
+
+i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
+vp = C.c_void_p
+i64, i32, f32 = C.c_int64, C.c_int32, C.c_float
+
+KV_BF16, KV_INT8 = 0, 1
+
+
+def load(path: str | None = None):
+    path = path or os.path.join(HERE, "liboracle.so")
+    if path in _LIBS:
+        return _LIBS[path]
+    if not os.path.exists(path):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("_oracle_build", os.path.join(HERE, "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build(path)
+    lib = C.CDLL(path)
+    paged = [vp, i64]                                     # block_table, stride_bt
+    geom = [i32, i32, i32, i64, i64, i64]                 # block_size, Hkv, D, strides
+    lib.oracle_prefill.argtypes = (
+        [vp, i64, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, f32, i32, i32,
+         u16p, vp, vp, vp, vp, i64, i64, i32p, i64, i32, f64p])
+    lib.oracle_prefill.restype = i32
+    lib.oracle_k_stats.argtypes = paged + [i32p, i32p, i32] + geom + [i32, vp, vp, i64, i64, f32p]
+    lib.oracle_k_stats.restype = i32
+    lib.oracle_k_quant.argtypes = paged + [i32p, i32p, i32] + geom + [i32, vp, vp, i64, i64, f32p, i8p]
+    lib.oracle_k_quant.restype = i32
+    lib.oracle_fp8_dense_dequant.argtypes = paged + [i32p, i32] + geom + [u8p, u8p, f32, f32, i32, u16p, u16p]
+    lib.oracle_fp8_dense_dequant.restype = i32
+    lib.oracle_gather_kv.argtypes = paged + [i32p, i32p, i32] + geom + [i32, vp, vp]
+    lib.oracle_gather_kv.restype = i32
+    lib.oracle_bf16_from_f32.argtypes = [f32p, u16p, i64]
+    lib.oracle_e4m3fn_to_f32.argtypes = [u8p, f32p, i64]
+    lib.oracle_max_threads.restype = i32
+    _LIBS[path] = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _pool_strides(pool):
+    nb, bs, hkv, d = pool.shape
+    return bs * hkv * d, hkv * d, d
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or load()).oracle_max_threads())
+
+
+# ------------------------------------------------------------------ attention
+def prefill(block_table, cu_q_lens, ctx_lens, q, k_pool, v_pool, softmax_scale,
+            num_kv_heads=None, causal=True, k_scales=None, v_scales=None, rows=None,
+            threads=0, lib=None):
+    """Attention of the listed chunk rows (all rows when None).  Returns
+    float64 [len(rows), Hq, D]."""
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cu_q = np.ascontiguousarray(cu_q_lens, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    nb, bs, hkv, d = k_pool.shape
+    hq = q.shape[1]
+    if rows is None:
+        rows = np.arange(int(cu_q[-1]), dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    out = np.empty((len(rows), hq, d), dtype=np.float64)
+    kind = KV_INT8 if k_pool.dtype == np.int8 else KV_BF16
+    if kind == KV_INT8:
+        ssb, sst = bs * hkv, hkv
+    else:
+        ssb = sst = 0
+    sb, st, sh = _pool_strides(k_pool)
+    rc = lib.oracle_prefill(_ptr(bt), bt.shape[1], cu_q, ctx, len(ctx), bs, hq, hkv, d,
+                            sb, st, sh, float(softmax_scale), int(bool(causal)), kind,
+                            np.ascontiguousarray(q), _ptr(k_pool), _ptr(v_pool),
+                            _ptr(k_scales), _ptr(v_scales), ssb, sst, rows, len(rows),
+                            int(threads), out)
+    if rc != 0:
+        raise ValueError(f"oracle_prefill failed ({rc})")
+    return out
+
+
+# ------------------------------------------------------------------ int8 K passes
+def k_stats(block_table, ctx_lens, k_pool, k_pool_scales=None, lib=None):
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    nb, bs, hkv, d = k_pool.shape
+    sb, st, sh = _pool_strides(k_pool)
+    kind = KV_INT8 if k_pool.dtype == np.int8 else KV_BF16
+    ks = np.empty((int(cu[-1]), hkv), dtype=np.float32)
+    lib.oracle_k_stats(_ptr(bt), bt.shape[1], ctx, cu, len(ctx), bs, hkv, d, sb, st, sh,
+                       kind, _ptr(k_pool), _ptr(k_pool_scales), bs * hkv, hkv, ks)
+    return ks
+
+
+def k_quant(block_table, ctx_lens, k_pool, ks, k_pool_scales=None, lib=None):
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    nb, bs, hkv, d = k_pool.shape
+    sb, st, sh = _pool_strides(k_pool)
+    kind = KV_INT8 if k_pool.dtype == np.int8 else KV_BF16
+    k8 = np.empty((int(cu[-1]), hkv, d), dtype=np.int8)
+    lib.oracle_k_quant(_ptr(bt), bt.shape[1], ctx, cu, len(ctx), bs, hkv, d, sb, st, sh,
+                       kind, _ptr(k_pool), _ptr(k_pool_scales), bs * hkv, hkv,
+                       np.ascontiguousarray(ks, dtype=np.float32), k8)
+    return k8
+
+
+# ------------------------------------------------------------------ fp8 dense dequant
+def fp8_dense_dequant(block_table, ctx_lens, k_pool, v_pool, k_scale, v_scale, max_seq, lib=None):
+    """Returns (k_scratch, v_scratch) uint16 [R, max_seq, Hkv, D]; positions at or
+    beyond each request's context are zero."""
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    nb, bs, hkv, d = k_pool.shape
+    sb, st, sh = _pool_strides(k_pool)
+    ksc = np.zeros((len(ctx), max_seq, hkv, d), dtype=np.uint16)
+    vsc = np.zeros_like(ksc)
+    rc = lib.oracle_fp8_dense_dequant(_ptr(bt), bt.shape[1], ctx, len(ctx), bs, hkv, d, sb, st,
+                                      sh, k_pool, v_pool, float(k_scale), float(v_scale),
+                                      int(max_seq), ksc, vsc)
+    if rc != 0:
+        raise ValueError("context longer than max_seq")
+    return ksc, vsc
+
+
+# ------------------------------------------------------------------ gather
+def gather_kv(block_table, ctx_lens, pool, lib=None):
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    nb, bs, hkv, d = pool.shape
+    sb, st, sh = _pool_strides(pool)
+    dense = np.empty((int(cu[-1]), hkv, d), dtype=pool.dtype)
+    lib.oracle_gather_kv(_ptr(bt), bt.shape[1], ctx, cu, len(ctx), bs, hkv, d, sb, st, sh,
+                         pool.dtype.itemsize, _ptr(pool), _ptr(dense))
+    return dense
+
+
+# ------------------------------------------------------------------ codecs
+def bf16_from_f32(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    load().oracle_bf16_from_f32(x.reshape(-1), y.reshape(-1), x.size)
+    return y
+
+
+def e4m3fn_to_f32(c):
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    y = np.empty(c.shape, dtype=np.float32)
+    load().oracle_e4m3fn_to_f32(c.reshape(-1), y.reshape(-1), c.size)
+    return y
+
+
+def bf16_bits_to_f64(b):
+    """bf16 bit patterns -> float64 values (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
