@@ -1,0 +1,186 @@
+/*
+ * paged_kv_prefill.h -- C ABI of the MI355X (gfx950) chunked-prefill attention
+ * library over a paged KV cache (libpaged_kv_prefill.so).
+ *
+ * The operation (HyperQwen PR #109, PR body and maintainer review): a query
+ * chunk of a request attends causally to the request's whole context, which
+ * sits in a paged KV pool.  Key/value position pos of request r lives in
+ * block  blk = block_table[r * stride_bt + pos / block_size]  at slot
+ * pos % block_size.  The element offset of (pos, kv head g, dim d) is
+ *     blk * stride_block + slot * stride_tok + g * stride_head + d
+ * and is always formed in 64-bit (HyperQwen PR #91, blocking review: with a
+ * block stride of 880 * 4 * 256 = 901,120 elements, block ids above 2,383
+ * overflow int32).  Chunk row i of request r sits at absolute position
+ * L_r - Lq_r + i and attends to keys 0..that position (bottom-right causal).
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Layouts (row-major, contiguous unless a stride says otherwise):
+ *   q, out       [sum_r Lq_r, num_q_heads, head_dim]   (bf16 in; fp32 or bf16 out)
+ *   K/V pools    [num_blocks, block_size, num_kv_heads, head_dim] via the strides
+ *   int8 scales  [num_blocks, block_size, num_kv_heads] via stride_sblock/stride_stok
+ *   dense k8     [sum_r L_r, num_kv_heads, head_dim] int8, ks [sum_r L_r, num_kv_heads]
+ *   fp8 scratch  [num_reqs, max_seq, num_kv_heads, head_dim] bf16
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer unless its comment says host.  The
+ *     pa_paged_args struct itself is read on the host during the call only.
+ *   - Every call is asynchronous on `stream`; nothing synchronises the host.
+ *   - The library allocates nothing and keeps no state between calls: all
+ *     buffers (outputs, the fp8 scratch, k8/ks intermediates) belong to the
+ *     caller and must stay alive until the stream work that uses them is done.
+ *   - Return value: PA_OK (0), or a negative PA_ERR_* code.  On an argument
+ *     error nothing is enqueued.  PA_ERR_LAUNCH means the launch itself failed
+ *     (hipGetLastError after the launch).  No C++ exception crosses the ABI.
+ *   - host-side bounds max_q_len / max_ctx_len size the grid: every device
+ *     length must respect them (rows beyond are not computed).  Requests whose
+ *     device lengths are inconsistent (Lq > L, L beyond what the block-table row
+ *     can hold, L > max_ctx_len) are skipped and their outputs left untouched.
+ *   - Block ids outside [0, num_blocks) are a caller error; the kernels read
+ *     such rows as zeros instead of touching memory outside the pool.
+ */
+#ifndef PAGED_KV_PREFILL_H
+#define PAGED_KV_PREFILL_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PA_OK               0
+#define PA_ERR_NULL        -1   /* a required pointer is NULL                     */
+#define PA_ERR_SHAPE       -2   /* inconsistent sizes or strides                  */
+#define PA_ERR_UNSUPPORTED -3   /* head_dim or dtype outside what is built        */
+#define PA_ERR_LAUNCH      -4   /* the kernel launch failed                       */
+#define PA_ERR_TOO_LARGE   -5   /* a size exceeds a documented maximum            */
+
+/* element types */
+#define PA_DTYPE_F32        0
+#define PA_DTYPE_BF16       1
+#define PA_DTYPE_INT8       2
+#define PA_DTYPE_FP8_E4M3   3   /* OCP e4m3fn: bias 7, no infinities, NaN = S.1111.111 */
+
+/* Problem description shared by all entry points (plain data, host memory). */
+typedef struct pa_paged_args {
+    const int32_t *block_table;   /* device int32 [num_reqs, stride_bt]                    */
+    int64_t stride_bt;            /* elements between block-table rows (>= blocks per req) */
+    const int32_t *cu_q_lens;     /* device int32 [num_reqs + 1], prefix sums of Lq_r      */
+    const int32_t *ctx_lens;      /* device int32 [num_reqs], L_r incl. the chunk          */
+    int32_t num_reqs;             /* >= 1                                                  */
+    int32_t max_q_len;            /* host bound: every Lq_r <= max_q_len                   */
+    int32_t max_ctx_len;          /* host bound: every L_r  <= max_ctx_len                 */
+    int32_t block_size;           /* tokens per block, >= 1                                */
+    int64_t num_blocks;           /* blocks in the pool                                    */
+    int32_t num_q_heads;          /* multiple of num_kv_heads                              */
+    int32_t num_kv_heads;
+    int32_t head_dim;             /* 64, 128 or 256                                        */
+    float softmax_scale;          /* logit scale, e.g. 1/sqrt(head_dim)                    */
+    int32_t causal;               /* 1: bottom-right causal; 0: every row sees all L keys  */
+    int64_t stride_block;         /* KV pool strides in elements                           */
+    int64_t stride_tok;
+    int64_t stride_head;
+    int64_t stride_sblock;        /* int8 per-token-head scale pool strides (elements)     */
+    int64_t stride_stok;
+} pa_paged_args;
+
+/*
+ * pa_prefill_bf16 -- chunked-prefill attention over a bf16 paged pool.
+ * (HyperQwen PR #109: the exact-QK arm of the int8 prefill kernel; vllm.cpp
+ * PR #3360: the bf16 dispatch that the fp8 scratch feeds.)
+ *   q        bf16 [sum Lq, Hq, D]
+ *   k_pool   bf16 pool, v_pool bf16 pool (same strides)
+ *   out      [sum Lq, Hq, D] of out_dtype (PA_DTYPE_F32 or PA_DTYPE_BF16)
+ * QK^T on bf16 MFMA and PV on fp16 MFMA, both with fp32 accumulation; the
+ * online softmax runs in fp32 and P is rounded to fp16 for PV.  V values must
+ * stay below 65520 in magnitude (fp16 range); larger ones give inf/NaN rows.
+ */
+int pa_prefill_bf16(const pa_paged_args *args, const void *q, const void *k_pool,
+                    const void *v_pool, void *out, int32_t out_dtype, hipStream_t stream);
+
+/*
+ * pa_prefill_int8kv -- the exact-QK arm over an int8 per-token-head pool
+ * (HyperQwen PR #91, first comment and merge review: int8_per_token_head KV,
+ * whose scale pointer is indexed by the same block id as the codes).
+ *   k_pool, v_pool    int8 codes
+ *   k_scales, v_scales fp32 [num_blocks, block_size, Hkv] (stride_sblock/stride_stok)
+ * Each element is dequantised in the tile from code * scale (fp32), rounded
+ * to bf16 for K and to fp16 for V, then the attention runs as pa_prefill_bf16.
+ */
+int pa_prefill_int8kv(const pa_paged_args *args, const void *q, const int8_t *k_pool,
+                      const int8_t *v_pool, const float *k_scales, const float *v_scales,
+                      void *out, int32_t out_dtype, hipStream_t stream);
+
+/*
+ * pa_k_stats -- first pass of the int8-QK prefill (HyperQwen PR #109: the
+ * K-stats kernel reads K through the block table).  For every context token
+ * t < L_r and KV head g:   ks[cu_ctx[r] + t, g] = max_d |K| / 127  (fp32).
+ *   k_pool        k_dtype PA_DTYPE_BF16 (bf16 pool) or PA_DTYPE_INT8 (codes)
+ *   k_pool_scales NULL for bf16; fp32 scale pool for int8 (K = code * scale in fp32)
+ *   cu_ctx        device int32 [num_reqs + 1], prefix sums of L_r
+ *   ks            fp32 [sum L, Hkv]
+ */
+int pa_k_stats(const pa_paged_args *args, const void *k_pool, int32_t k_dtype,
+               const float *k_pool_scales, const int32_t *cu_ctx, float *ks,
+               hipStream_t stream);
+
+/*
+ * pa_k_quant -- second pass (HyperQwen PR #109: the K-quant kernel writes int8
+ * K into a buffer indexed by position).  k8[cu_ctx[r] + t, g, d] =
+ * clamp(round_half_even(K / ks), -127, 127), 0 where ks == 0; fp32 division.
+ *   k8  int8 [sum L, Hkv, D]
+ */
+int pa_k_quant(const pa_paged_args *args, const void *k_pool, int32_t k_dtype,
+               const float *k_pool_scales, const int32_t *cu_ctx, const float *ks,
+               int8_t *k8, hipStream_t stream);
+
+/*
+ * pa_prefill_int8qk -- the int8-QK arm (HyperQwen PR #109, int8_qk=True): Q is
+ * quantised per (token, q head) in the prologue (sq = max|q| / 127, codes
+ * rounded half-even), S = float(int8 dot, int32 accumulate) * sq * ks * scale,
+ * then fp32 online softmax and bf16 PV.
+ *   k8, ks     outputs of pa_k_quant / pa_k_stats, indexed by position
+ *   v_pool     v_dtype PA_DTYPE_BF16 (bf16 pool) or PA_DTYPE_INT8 (codes, with v_scales)
+ */
+int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8,
+                      const float *ks, const int32_t *cu_ctx, const void *v_pool,
+                      int32_t v_dtype, const float *v_scales, void *out, int32_t out_dtype,
+                      hipStream_t stream);
+
+/*
+ * pa_fp8_dense_dequant -- one-time dense dequant of an fp8 paged pool
+ * (vllm.cpp PR #3360, "What changed": the fp8 cache is dequantised once into
+ * a dense bf16 scratch of one block per request with block_size = max_seq, so
+ * that an identity block table addresses it and the bf16 attention runs on it
+ * unchanged).  For t < L_r:
+ *     k_scratch[r, t, g, d] = bf16_rne(fp32(e4m3fn(code)) * (*k_scale))
+ * and likewise for V.  k_scale / v_scale are DEVICE fp32 scalars (one scale per
+ * tensor).  Positions t >= L_r of the scratch are not written.  Afterwards call
+ * pa_prefill_bf16 with block_size = max_seq, block_table row r = {r},
+ * stride_block = max_seq * Hkv * D, stride_tok = Hkv * D, stride_head = D.
+ */
+int pa_fp8_dense_dequant(const pa_paged_args *args, const uint8_t *k_pool,
+                         const uint8_t *v_pool, const float *k_scale, const float *v_scale,
+                         int32_t max_seq, void *k_scratch, void *v_scratch,
+                         hipStream_t stream);
+
+/*
+ * pa_gather_kv -- test export: copy a paged pool's rows to a dense buffer by
+ * position, dense[cu_ctx[r] + t, g, :] = pool row (r, t, g), elem_bytes 1 or 2.
+ * Exercises the same 64-bit block addressing as the attention kernels.
+ */
+int pa_gather_kv(const pa_paged_args *args, const void *pool, int32_t elem_bytes,
+                 const int32_t *cu_ctx, void *dense, hipStream_t stream);
+
+/* Human-readable text of a status code (static storage). */
+const char *pa_status_string(int32_t status);
+
+/* Identifier of this build (source hash and compile flags; static storage). */
+const char *pa_build_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PREFILL_H */

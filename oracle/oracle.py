@@ -48,6 +48,10 @@ def load(path: str | None = None):
         [vp, i64, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, f32, i32, i32,
          u16p, vp, vp, vp, vp, i64, i64, i32p, i64, i32, f64p])
     lib.oracle_prefill.restype = i32
+    lib.oracle_prefill_int8qk.argtypes = (
+        [vp, i64, i32p, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, f32, i32, i32,
+         u16p, i8p, f32p, vp, vp, i64, i64, i32p, i64, i32, f64p])
+    lib.oracle_prefill_int8qk.restype = i32
     lib.oracle_k_stats.argtypes = paged + [i32p, i32p, i32] + geom + [i32, vp, vp, i64, i64, f32p]
     lib.oracle_k_stats.restype = i32
     lib.oracle_k_quant.argtypes = paged + [i32p, i32p, i32] + geom + [i32, vp, vp, i64, i64, f32p, i8p]
@@ -105,6 +109,35 @@ def prefill(block_table, cu_q_lens, ctx_lens, q, k_pool, v_pool, softmax_scale,
                             int(threads), out)
     if rc != 0:
         raise ValueError(f"oracle_prefill failed ({rc})")
+    return out
+
+
+def prefill_int8qk(block_table, cu_q_lens, ctx_lens, q, k8, ks, v_pool, softmax_scale,
+                   causal=True, v_scales=None, rows=None, threads=0, lib=None):
+    """The int8-QK arm with its quantisation steps taken exactly as the method
+    defines them (k8 / ks from k_quant / k_stats).  Returns float64
+    [len(rows), Hq, D]."""
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cu_q = np.ascontiguousarray(cu_q_lens, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    cu_ctx = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    nb, bs, hkv, d = v_pool.shape
+    hq = q.shape[1]
+    if rows is None:
+        rows = np.arange(int(cu_q[-1]), dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    out = np.empty((len(rows), hq, d), dtype=np.float64)
+    vkind = KV_INT8 if v_pool.dtype == np.int8 else KV_BF16
+    sb, st, sh = _pool_strides(v_pool)
+    rc = lib.oracle_prefill_int8qk(_ptr(bt), bt.shape[1], cu_q, ctx, cu_ctx, len(ctx), bs, hq, hkv,
+                                   d, sb, st, sh, float(softmax_scale), int(bool(causal)), vkind,
+                                   np.ascontiguousarray(q), np.ascontiguousarray(k8),
+                                   np.ascontiguousarray(ks, dtype=np.float32), _ptr(v_pool),
+                                   _ptr(v_scales), bs * hkv, hkv, rows, len(rows), int(threads),
+                                   out)
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_int8qk failed ({rc})")
     return out
 
 

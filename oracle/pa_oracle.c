@@ -33,6 +33,10 @@
  *    where x is the fp32 K value (bf16, or code * scale rounded once in fp32).
  *    These are integer decisions taken in fp32, the precision the GPU uses.
  *
+ *  - int8-QK arm (same PR, int8_qk=True): Q quantised per (token, head) like
+ *    K, logits from the exact integer dot of the codes times sq * ks * scale,
+ *    then softmax and PV in double precision.
+ *
  *  - fp8 dense dequant (vllm.cpp PR #3360, "What changed"): the fp8 cache is
  *    dequantised once into a dense bf16 scratch with one block per request of
  *    block_size = max_seq, so that an identity block table addresses it:
@@ -221,6 +225,101 @@ int oracle_prefill(const int32_t *block_table, int64_t stride_bt,
         }
         free(s);
         free(qv);
+        free(acc);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------ int8-QK arm */
+
+/* The int8-QK arm of the int8 prefill (HyperQwen PR #109, int8_qk=True) as the
+ * method defines it, evaluated exactly after its quantisation steps: each
+ * query row (token, q head) is quantised like K, sq = max_d|q| / 127 and
+ * q8 = clamp(round_half_even(q / sq), -127, 127) in fp32; the logit of key j
+ * is  scale * sq * ks[j] * sum_d q8[d] * k8[j, d]  (the integer dot is exact);
+ * softmax and PV follow in double precision.  k8 / ks are the outputs of the
+ * K-quant / K-stats passes, indexed by cu_ctx[r] + position.  V is a bf16
+ * pool (v_kind 0) or an int8 pool with per-token-head scales (v_kind 1). */
+int oracle_prefill_int8qk(const int32_t *block_table, int64_t stride_bt,
+                          const int32_t *cu_q_lens, const int32_t *ctx_lens,
+                          const int32_t *cu_ctx, int32_t num_reqs, int32_t block_size,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int64_t stride_block, int64_t stride_tok, int64_t stride_head,
+                          float softmax_scale, int32_t causal, int32_t v_kind,
+                          const uint16_t *q, const int8_t *k8, const float *ks,
+                          const void *v_pool, const float *v_scales, int64_t stride_sblock,
+                          int64_t stride_stok, const int32_t *rows, int64_t num_rows,
+                          int32_t num_threads, double *out) {
+    if (num_q_heads % num_kv_heads != 0 || block_size < 1 || head_dim < 1)
+        return -1;
+    paged_view pv = {block_table, stride_bt, block_size, stride_block, stride_tok, stride_head};
+    const int group = num_q_heads / num_kv_heads;
+    const int D = head_dim;
+    int32_t max_ctx = 0;
+    for (int r = 0; r < num_reqs; ++r)
+        if (ctx_lens[r] > max_ctx) max_ctx = ctx_lens[r];
+    int bad = 0;
+    set_threads(num_threads);
+
+#pragma omp parallel reduction(| : bad)
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(max_ctx > 0 ? max_ctx : 1));
+        int32_t *q8 = (int32_t *)malloc(sizeof(int32_t) * (size_t)D);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t w = 0; w < num_rows * num_q_heads; ++w) {
+            int64_t row = rows[w / num_q_heads];
+            int h = (int)(w % num_q_heads);
+            int r = 0;
+            while (r < num_reqs && !(cu_q_lens[r] <= row && row < cu_q_lens[r + 1])) ++r;
+            double *o = out + w * D;
+            if (r == num_reqs) { bad = 1; continue; }
+            int64_t qlen = cu_q_lens[r + 1] - cu_q_lens[r];
+            int64_t L = ctx_lens[r];
+            int64_t p = L - qlen + (row - cu_q_lens[r]);
+            int64_t nkeys = causal ? p + 1 : L;
+            int g = h / group;
+            const uint16_t *qr = q + (row * num_q_heads + h) * (int64_t)D;
+            float amax = 0.0f;
+            for (int d = 0; d < D; ++d) {
+                float x = fabsf(bf16_bits_to_f32(qr[d]));
+                if (x > amax) amax = x;
+            }
+            float sq = amax / 127.0f;
+            for (int d = 0; d < D; ++d) {
+                float y = sq != 0.0f ? nearbyintf(bf16_bits_to_f32(qr[d]) / sq) : 0.0f;
+                if (y > 127.0f) y = 127.0f;
+                if (y < -127.0f) y = -127.0f;
+                q8[d] = (int32_t)y;
+            }
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                int64_t krow = ((int64_t)cu_ctx[r] + j) * num_kv_heads + g;
+                const int8_t *kp = k8 + krow * D;
+                int64_t dot = 0;
+                for (int d = 0; d < D; ++d) dot += (int64_t)q8[d] * (int64_t)kp[d];
+                s[j] = (double)softmax_scale * (double)sq * (double)ks[krow] * (double)dot;
+                if (s[j] > m) m = s[j];
+            }
+            double l = 0.0;
+            for (int d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                double e = exp(s[j] - m);
+                l += e;
+                int64_t off = paged_offset(&pv, r, j, g);
+                if (v_kind == KV_BF16) {
+                    const uint16_t *vp = (const uint16_t *)v_pool + off;
+                    for (int d = 0; d < D; ++d) acc[d] += e * (double)bf16_bits_to_f32(vp[d]);
+                } else {
+                    const int8_t *vp = (const int8_t *)v_pool + off;
+                    double sc = (double)v_scales[scale_offset(&pv, stride_sblock, stride_stok, r, j, g)];
+                    for (int d = 0; d < D; ++d) acc[d] += e * ((double)vp[d] * sc);
+                }
+            }
+            for (int d = 0; d < D; ++d) o[d] = nkeys > 0 ? acc[d] / l : 0.0;
+        }
+        free(s);
+        free(q8);
         free(acc);
     }
     return bad ? -2 : 0;

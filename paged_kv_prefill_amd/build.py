@@ -1,0 +1,72 @@
+"""Build libpaged_kv_prefill.so (gfx950) in-tree with hipcc.
+
+    python -m paged_kv_prefill_amd.build     (or build() from Python)
+
+Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
+selection disabled, no fast-math (IEEE division and rounding are needed for
+bit-exact int8 codes and fp8 dequant), and a build id made of the sources'
+hash and the flags.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import hashlib
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libpaged_kv_prefill.so")
+SOURCES = ["pa_attention.hip", "pa_passes.hip", "pa_api.cpp"]
+HEADERS = ["pa_device.h", "pa_kernels.h"]
+PUBLIC_HEADER = os.path.join(ROOT, "include", "paged_kv_prefill.h")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+
+
+def _source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SOURCES + HEADERS:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(PUBLIC_HEADER, "rb") as fh:
+        h.update(fh.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    bid = f"paged_kv_prefill gfx950 src={_source_hash()}"
+    defs = [f'-DPA_BUILD_ID="{bid}"']
+
+    def compile_one(src):
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC] + FLAGS + defs + ["-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+        msgs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+        if verbose and msgs.strip():
+            print(msgs)
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    import time
+    t = time.time()
+    print(build(verbose=True), f"{time.time() - t:.1f}s")

@@ -1,0 +1,256 @@
+// pa_api.cpp -- the C ABI (include/paged_kv_prefill.h): argument checks, kernel
+// parameter blocks, launches.  Allocates nothing, never synchronises the host.
+#include "../../include/paged_kv_prefill.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_kernels.h"
+
+#ifndef PA_BUILD_ID
+#define PA_BUILD_ID "unversioned"
+#endif
+
+using namespace pa;
+
+namespace {
+
+FastDivHost make_fastdiv(uint32_t d) {
+    uint32_t shift = 0;
+    while ((1ull << shift) < d) ++shift;
+    uint64_t mul = ((1ull << 32) * ((1ull << shift) - d)) / d + 1;
+    return FastDivHost{(uint32_t)mul, shift, d};
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by every entry point.  elem_bytes: bytes per pool element.
+int check_common(const pa_paged_args *a, int elem_bytes, bool needs_q) {
+    if (!a) return PA_ERR_NULL;
+    if (!a->block_table || !a->ctx_lens || (needs_q && !a->cu_q_lens)) return PA_ERR_NULL;
+    if (a->num_reqs < 1 || a->block_size < 1 || a->num_blocks < 1 || a->num_kv_heads < 1 ||
+        a->num_q_heads < 1 || a->stride_bt < 1)
+        return PA_ERR_SHAPE;
+    if (a->num_q_heads % a->num_kv_heads != 0) return PA_ERR_SHAPE;
+    if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256) return PA_ERR_UNSUPPORTED;
+    if (a->max_ctx_len < 0 || a->max_q_len < 0 || (needs_q && a->max_q_len > a->max_ctx_len))
+        return PA_ERR_SHAPE;
+    if (a->causal != 0 && a->causal != 1) return PA_ERR_SHAPE;
+    if (a->stride_block < 1 || a->stride_tok < 1 || a->stride_head < 1) return PA_ERR_SHAPE;
+    // rows are read as 16-byte vectors: every row start must be 16-byte aligned
+    const int64_t q16 = 16 / elem_bytes;
+    if (a->stride_block % q16 || a->stride_tok % q16 || a->stride_head % q16) return PA_ERR_SHAPE;
+    // a request's chunk-position arithmetic is int32 (positions < 2^31)
+    if ((int64_t)a->max_ctx_len * a->num_kv_heads >= ((int64_t)1 << 31)) return PA_ERR_TOO_LARGE;
+    return PA_OK;
+}
+
+AttnParams attn_params(const pa_paged_args *a) {
+    AttnParams p{};
+    p.bt = a->block_table;
+    p.stride_bt = a->stride_bt;
+    p.cu_q = a->cu_q_lens;
+    p.ctx_lens = a->ctx_lens;
+    p.num_reqs = a->num_reqs;
+    p.Hq = a->num_q_heads;
+    p.Hkv = a->num_kv_heads;
+    p.group = a->num_q_heads / a->num_kv_heads;
+    p.block_size = a->block_size;
+    p.max_ctx = a->max_ctx_len;
+    p.bsdiv = make_fastdiv((uint32_t)a->block_size);
+    p.num_blocks = a->num_blocks;
+    p.stride_block = a->stride_block;
+    p.stride_tok = a->stride_tok;
+    p.stride_head = a->stride_head;
+    p.stride_sblock = a->stride_sblock;
+    p.stride_stok = a->stride_stok;
+    p.scale = a->softmax_scale;
+    p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+    p.causal = a->causal;
+    return p;
+}
+
+PassParams pass_params(const pa_paged_args *a) {
+    PassParams p{};
+    p.bt = a->block_table;
+    p.stride_bt = a->stride_bt;
+    p.ctx_lens = a->ctx_lens;
+    p.num_reqs = a->num_reqs;
+    p.Hkv = a->num_kv_heads;
+    p.D = a->head_dim;
+    p.block_size = a->block_size;
+    p.max_ctx = a->max_ctx_len;
+    p.bsdiv = make_fastdiv((uint32_t)a->block_size);
+    p.num_blocks = a->num_blocks;
+    p.stride_block = a->stride_block;
+    p.stride_tok = a->stride_tok;
+    p.stride_head = a->stride_head;
+    p.stride_sblock = a->stride_sblock;
+    p.stride_stok = a->stride_stok;
+    return p;
+}
+
+int check_out(const void *q, void *out, int32_t out_dtype) {
+    if (!q || !out) return PA_ERR_NULL;
+    if (out_dtype != PA_DTYPE_F32 && out_dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out)) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+int check_scales(const pa_paged_args *a, const float *s) {
+    if (!s) return PA_ERR_NULL;
+    if (a->stride_sblock < 1 || a->stride_stok < 1) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
+                    void *out, int32_t out_dtype, hipStream_t stream) {
+    int rc = check_common(a, 2, true);
+    if (rc) return rc;
+    if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (!k_pool || !v_pool) return PA_ERR_NULL;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    AttnParams p = attn_params(a);
+    p.q = q;
+    p.k = k_pool;
+    p.v = v_pool;
+    p.out = out;
+    return launched(launch_attention(KIND_BF16, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
+                                     a->max_q_len, stream));
+}
+
+int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
+                      const int8_t *v_pool, const float *k_scales, const float *v_scales,
+                      void *out, int32_t out_dtype, hipStream_t stream) {
+    int rc = check_common(a, 1, true);
+    if (rc) return rc;
+    if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (!k_pool || !v_pool) return PA_ERR_NULL;
+    if ((rc = check_scales(a, k_scales)) || (rc = check_scales(a, v_scales))) return rc;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    AttnParams p = attn_params(a);
+    p.q = q;
+    p.k = k_pool;
+    p.v = v_pool;
+    p.kscale = k_scales;
+    p.vscale = v_scales;
+    p.out = out;
+    return launched(launch_attention(KIND_I8KV, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
+                                     a->max_q_len, stream));
+}
+
+int pa_k_stats(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
+               const float *k_pool_scales, const int32_t *cu_ctx, float *ks, hipStream_t stream) {
+    if (k_dtype != PA_DTYPE_BF16 && k_dtype != PA_DTYPE_INT8) return PA_ERR_UNSUPPORTED;
+    int rc = check_common(a, k_dtype == PA_DTYPE_INT8 ? 1 : 2, false);
+    if (rc) return rc;
+    if (!k_pool || !cu_ctx || !ks) return PA_ERR_NULL;
+    if (k_dtype == PA_DTYPE_INT8 && (rc = check_scales(a, k_pool_scales))) return rc;
+    if (!aligned16(k_pool)) return PA_ERR_SHAPE;
+    PassParams p = pass_params(a);
+    p.cu_ctx = cu_ctx;
+    p.src = k_pool;
+    p.src_int8 = k_dtype == PA_DTYPE_INT8;
+    p.src_scales = k_pool_scales;
+    p.dst = ks;
+    return launched(launch_k_stats(p, stream));
+}
+
+int pa_k_quant(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
+               const float *k_pool_scales, const int32_t *cu_ctx, const float *ks, int8_t *k8,
+               hipStream_t stream) {
+    if (k_dtype != PA_DTYPE_BF16 && k_dtype != PA_DTYPE_INT8) return PA_ERR_UNSUPPORTED;
+    int rc = check_common(a, k_dtype == PA_DTYPE_INT8 ? 1 : 2, false);
+    if (rc) return rc;
+    if (!k_pool || !cu_ctx || !ks || !k8) return PA_ERR_NULL;
+    if (k_dtype == PA_DTYPE_INT8 && (rc = check_scales(a, k_pool_scales))) return rc;
+    if (!aligned16(k_pool) || !aligned16(k8)) return PA_ERR_SHAPE;
+    PassParams p = pass_params(a);
+    p.cu_ctx = cu_ctx;
+    p.src = k_pool;
+    p.src_int8 = k_dtype == PA_DTYPE_INT8;
+    p.src_scales = k_pool_scales;
+    p.ks = ks;
+    p.dst = k8;
+    return launched(launch_k_quant(p, stream));
+}
+
+int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, const float *ks,
+                      const int32_t *cu_ctx, const void *v_pool, int32_t v_dtype,
+                      const float *v_scales, void *out, int32_t out_dtype, hipStream_t stream) {
+    if (v_dtype != PA_DTYPE_BF16 && v_dtype != PA_DTYPE_INT8) return PA_ERR_UNSUPPORTED;
+    int rc = check_common(a, v_dtype == PA_DTYPE_INT8 ? 1 : 2, true);
+    if (rc) return rc;
+    if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (!k8 || !ks || !cu_ctx || !v_pool) return PA_ERR_NULL;
+    if (v_dtype == PA_DTYPE_INT8 && (rc = check_scales(a, v_scales))) return rc;
+    if (!aligned16(k8) || !aligned16(ks) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    AttnParams p = attn_params(a);
+    p.cu_ctx = cu_ctx;
+    p.q = q;
+    p.k = k8;
+    p.kscale = ks;
+    p.v = v_pool;
+    p.vscale = v_scales;
+    p.out = out;
+    const int kind = v_dtype == PA_DTYPE_INT8 ? KIND_QK8_VI8 : KIND_QK8_VBF16;
+    return launched(launch_attention(kind, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
+                                     a->max_q_len, stream));
+}
+
+int pa_fp8_dense_dequant(const pa_paged_args *a, const uint8_t *k_pool, const uint8_t *v_pool,
+                         const float *k_scale, const float *v_scale, int32_t max_seq,
+                         void *k_scratch, void *v_scratch, hipStream_t stream) {
+    int rc = check_common(a, 1, false);
+    if (rc) return rc;
+    if (!k_pool || !v_pool || !k_scale || !v_scale || !k_scratch || !v_scratch) return PA_ERR_NULL;
+    if (max_seq < 1 || max_seq < a->max_ctx_len) return PA_ERR_SHAPE;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_scratch) || !aligned16(v_scratch))
+        return PA_ERR_SHAPE;
+    PassParams p = pass_params(a);
+    p.src = k_pool;
+    p.src2 = v_pool;
+    p.fscale = k_scale;
+    p.fscale2 = v_scale;
+    p.dst = k_scratch;
+    p.dst2 = v_scratch;
+    p.max_seq = max_seq;
+    return launched(launch_fp8_dequant(p, stream));
+}
+
+int pa_gather_kv(const pa_paged_args *a, const void *pool, int32_t elem_bytes,
+                 const int32_t *cu_ctx, void *dense, hipStream_t stream) {
+    if (elem_bytes != 1 && elem_bytes != 2) return PA_ERR_UNSUPPORTED;
+    int rc = check_common(a, elem_bytes, false);
+    if (rc) return rc;
+    if (!pool || !cu_ctx || !dense) return PA_ERR_NULL;
+    if (!aligned16(pool) || !aligned16(dense)) return PA_ERR_SHAPE;
+    PassParams p = pass_params(a);
+    p.cu_ctx = cu_ctx;
+    p.src = pool;
+    p.dst = dense;
+    p.elem_bytes = elem_bytes;
+    return launched(launch_gather(p, stream));
+}
+
+const char *pa_status_string(int32_t status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL: return "a required pointer is NULL";
+        case PA_ERR_SHAPE: return "inconsistent sizes, strides or alignment";
+        case PA_ERR_UNSUPPORTED: return "head_dim or dtype not supported";
+        case PA_ERR_LAUNCH: return "kernel launch failed";
+        case PA_ERR_TOO_LARGE: return "size above the supported maximum";
+        default: return "unknown status";
+    }
+}
+
+const char *pa_build_id(void) { return PA_BUILD_ID; }
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// pa_kernels.h -- kernel parameter blocks and launchers (host and device).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct FastDivHost {
+    uint32_t mul, shift, d;
+};
+
+// Attention kernels: every pointer is device memory.
+struct AttnParams {
+    const int32_t *bt;
+    int64_t stride_bt;
+    const int32_t *cu_q;
+    const int32_t *ctx_lens;
+    const int32_t *cu_ctx;      // int8-QK only: prefix sums of L (k8/ks rows)
+    int32_t num_reqs, Hq, Hkv, group;
+    int32_t block_size, max_ctx;
+    FastDivHost bsdiv;
+    int64_t num_blocks;
+    int64_t stride_block, stride_tok, stride_head;
+    int64_t stride_sblock, stride_stok;
+    float scale;                // softmax scale
+    float scale_log2;           // softmax scale * log2(e)
+    int32_t causal;
+    int32_t tiles;              // column tiles per (request, kv head)
+    const void *q;
+    const void *k;              // bf16 / int8 pool, or dense k8
+    const void *v;              // bf16 / int8 pool
+    const float *kscale;        // int8 pool scales, or ks (int8-QK)
+    const float *vscale;
+    void *out;
+};
+
+enum AttnKind { KIND_BF16 = 0, KIND_I8KV = 1, KIND_QK8_VBF16 = 2, KIND_QK8_VI8 = 3 };
+
+// Per-token passes (K stats, K quant, fp8 dense dequant, gather).
+struct PassParams {
+    const int32_t *bt;
+    int64_t stride_bt;
+    const int32_t *ctx_lens;
+    const int32_t *cu_ctx;
+    int32_t num_reqs, Hkv, D, block_size, max_ctx;
+    FastDivHost bsdiv;
+    int64_t num_blocks;
+    int64_t stride_block, stride_tok, stride_head;
+    int64_t stride_sblock, stride_stok;
+    const void *src;            // pool (K, or K of the fp8 pair)
+    const void *src2;           // V of the fp8 pair
+    const float *src_scales;    // int8 pool scales
+    const float *ks;            // K-quant input scales
+    const float *fscale;        // fp8 per-tensor scales (device scalars): K
+    const float *fscale2;       //                                        V
+    void *dst;
+    void *dst2;
+    int32_t max_seq;            // fp8 scratch rows per request
+    int32_t elem_bytes;         // gather
+    int32_t src_int8;           // K passes: 1 int8 pool, 0 bf16 pool
+};
+
+// launchers: return hipError_t of the launch
+hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,
+                            int32_t max_q_len, hipStream_t stream);
+hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);
+hipError_t launch_k_quant(const PassParams &p, hipStream_t stream);
+hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t stream);
+hipError_t launch_gather(const PassParams &p, hipStream_t stream);
+
+constexpr int ATTN_THREADS = 256;
+constexpr int ATTN_COLS = 128;   // (token, q head) columns per workgroup
+
+}  // namespace pa

@@ -1,0 +1,218 @@
+"""ctypes binding of libpaged_kv_prefill.so (argument marshalling only).
+
+The entry points keep the C names of include/paged_kv_prefill.h.  Tensors are
+torch tensors used only as device memory; the launch goes on torch's current
+stream.  Nothing here computes: if the library is missing, loading fails
+loudly (build it with `python -m paged_kv_prefill_amd.build`).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpaged_kv_prefill.so")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_INT8, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
+
+ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_k_stats", "pa_k_quant",
+                "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_gather_kv",
+                "pa_status_string", "pa_build_id"]
+
+
+class PagedArgs(C.Structure):
+    """Mirror of pa_paged_args."""
+    _fields_ = [
+        ("block_table", C.c_void_p), ("stride_bt", C.c_int64),
+        ("cu_q_lens", C.c_void_p), ("ctx_lens", C.c_void_p),
+        ("num_reqs", C.c_int32), ("max_q_len", C.c_int32), ("max_ctx_len", C.c_int32),
+        ("block_size", C.c_int32), ("num_blocks", C.c_int64),
+        ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("softmax_scale", C.c_float), ("causal", C.c_int32),
+        ("stride_block", C.c_int64), ("stride_tok", C.c_int64), ("stride_head", C.c_int64),
+        ("stride_sblock", C.c_int64), ("stride_stok", C.c_int64),
+    ]
+
+
+class PagedKVError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is not built; run `python -m paged_kv_prefill_amd.build` "
+                "(there is no CPU fallback)")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, pa = C.c_void_p, C.c_int32, C.POINTER(PagedArgs)
+        sig = {
+            "pa_prefill_bf16": [pa, vp, vp, vp, vp, i32, vp],
+            "pa_prefill_int8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp],
+            "pa_k_stats": [pa, vp, i32, vp, vp, vp, vp],
+            "pa_k_quant": [pa, vp, i32, vp, vp, vp, vp, vp],
+            "pa_prefill_int8qk": [pa, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp],
+            "pa_fp8_dense_dequant": [pa, vp, vp, vp, vp, i32, vp, vp, vp],
+            "pa_gather_kv": [pa, vp, i32, vp, vp, vp],
+        }
+        for name, argt in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = argt
+            fn.restype = i32
+        L.pa_status_string.argtypes = [i32]
+        L.pa_status_string.restype = C.c_char_p
+        L.pa_build_id.argtypes = []
+        L.pa_build_id.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def build_id() -> str:
+    return lib().pa_build_id().decode()
+
+
+def status_string(code: int) -> str:
+    return lib().pa_status_string(int(code)).decode()
+
+
+def _check(rc: int, name: str):
+    if rc != PA_OK:
+        raise PagedKVError(f"{name} returned {rc}: {status_string(rc)}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Paged:
+    """Device-side problem description: keeps the tensors that pa_paged_args
+    points at alive and builds the struct."""
+    block_table: torch.Tensor          # int32 [R, stride_bt]
+    cu_q_lens: torch.Tensor            # int32 [R+1]
+    ctx_lens: torch.Tensor             # int32 [R]
+    max_q_len: int
+    max_ctx_len: int
+    block_size: int
+    num_blocks: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    softmax_scale: float
+    causal: bool = True
+    stride_block: Optional[int] = None
+    stride_tok: Optional[int] = None
+    stride_head: Optional[int] = None
+
+    def args(self) -> PagedArgs:
+        hkv, d, bs = self.num_kv_heads, self.head_dim, self.block_size
+        a = PagedArgs()
+        a.block_table = self.block_table.data_ptr()
+        bt = self.block_table
+        if bt.dim() != 2 or bt.stride(1) != 1:
+            raise ValueError("block_table must be a 2-D int32 tensor with unit column stride")
+        # a size-1 leading dimension may carry any stride (even 0); use the row length then
+        a.stride_bt = bt.stride(0) if bt.shape[0] > 1 else bt.shape[1]
+        a.cu_q_lens = self.cu_q_lens.data_ptr()
+        a.ctx_lens = self.ctx_lens.data_ptr()
+        a.num_reqs = self.ctx_lens.numel()
+        a.max_q_len = self.max_q_len
+        a.max_ctx_len = self.max_ctx_len
+        a.block_size = bs
+        a.num_blocks = self.num_blocks
+        a.num_q_heads = self.num_q_heads
+        a.num_kv_heads = hkv
+        a.head_dim = d
+        a.softmax_scale = self.softmax_scale
+        a.causal = int(bool(self.causal))
+        a.stride_block = self.stride_block if self.stride_block is not None else bs * hkv * d
+        a.stride_tok = self.stride_tok if self.stride_tok is not None else hkv * d
+        a.stride_head = self.stride_head if self.stride_head is not None else d
+        a.stride_sblock = bs * hkv
+        a.stride_stok = hkv
+        return a
+
+
+# ------------------------------------------------------------------ entry points
+def pa_prefill_bf16(p: Paged, q, k_pool, v_pool, out, stream=None):
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    _check(lib().pa_prefill_bf16(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(out), dt,
+                                 _stream(stream)), "pa_prefill_bf16")
+    return out
+
+
+def pa_prefill_int8kv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, out, stream=None):
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    _check(lib().pa_prefill_int8kv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(k_scales),
+                                   _p(v_scales), _p(out), dt, _stream(stream)),
+           "pa_prefill_int8kv")
+    return out
+
+
+def _kdtype(pool):
+    return PA_DTYPE_INT8 if pool.dtype == torch.int8 else PA_DTYPE_BF16
+
+
+def pa_k_stats(p: Paged, k_pool, k_pool_scales, cu_ctx, ks, stream=None):
+    a = p.args()
+    _check(lib().pa_k_stats(C.byref(a), _p(k_pool), _kdtype(k_pool), _p(k_pool_scales),
+                            _p(cu_ctx), _p(ks), _stream(stream)), "pa_k_stats")
+    return ks
+
+
+def pa_k_quant(p: Paged, k_pool, k_pool_scales, cu_ctx, ks, k8, stream=None):
+    a = p.args()
+    _check(lib().pa_k_quant(C.byref(a), _p(k_pool), _kdtype(k_pool), _p(k_pool_scales),
+                            _p(cu_ctx), _p(ks), _p(k8), _stream(stream)), "pa_k_quant")
+    return k8
+
+
+def pa_prefill_int8qk(p: Paged, q, k8, ks, cu_ctx, v_pool, v_scales, out, stream=None):
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    _check(lib().pa_prefill_int8qk(C.byref(a), _p(q), _p(k8), _p(ks), _p(cu_ctx), _p(v_pool),
+                                   _kdtype(v_pool), _p(v_scales), _p(out), dt, _stream(stream)),
+           "pa_prefill_int8qk")
+    return out
+
+
+def pa_fp8_dense_dequant(p: Paged, k_pool, v_pool, k_scale, v_scale, max_seq, k_scratch,
+                         v_scratch, stream=None):
+    a = p.args()
+    _check(lib().pa_fp8_dense_dequant(C.byref(a), _p(k_pool), _p(v_pool), _p(k_scale),
+                                      _p(v_scale), int(max_seq), _p(k_scratch), _p(v_scratch),
+                                      _stream(stream)), "pa_fp8_dense_dequant")
+    return k_scratch, v_scratch
+
+
+def pa_gather_kv(p: Paged, pool, cu_ctx, dense, stream=None):
+    a = p.args()
+    _check(lib().pa_gather_kv(C.byref(a), _p(pool), pool.element_size(), _p(cu_ctx), _p(dense),
+                              _stream(stream)), "pa_gather_kv")
+    return dense
+
+
+def scratch_view(p: Paged, max_seq: int, device) -> Paged:
+    """Problem description for attention over the dense fp8 scratch: one block
+    per request of block_size = max_seq, identity block table."""
+    R = p.ctx_lens.numel()
+    ident = torch.arange(R, dtype=torch.int32, device=device).reshape(R, 1)
+    return Paged(ident, p.cu_q_lens, p.ctx_lens, p.max_q_len, p.max_ctx_len, max_seq, R,
+                 p.num_q_heads, p.num_kv_heads, p.head_dim, p.softmax_scale, p.causal)

@@ -1,0 +1,151 @@
+"""Device-side construction of seeded workloads for the GPU parity tests, and
+the matching host pools for the oracle.  Plumbing only: torch is used for
+device memory and copies; every computation goes through the C ABI."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from paged_kv_prefill_amd import ops, synth
+
+DEV = "cuda"
+
+
+def dev_bf16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16_to_np(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DevCase:
+    """Device pools holding a workload at one or more placements (block
+    tables), poisoned everywhere else, plus its Q and metadata."""
+
+    def __init__(self, w: synth.Workload, tables=None):
+        self.w = w
+        tables = [w.block_table] if tables is None else tables
+        self.tables = [np.ascontiguousarray(t, dtype=np.int32) for t in tables]
+        self.cu_q = dev(w.cu_q_lens)
+        self.ctx = dev(w.ctx_lens)
+        self.cu_ctx = dev(w.cu_ctx_lens)
+        self.q = dev_bf16(w.q)
+        shape = w.pool_shape
+        self.k_scales = self.v_scales = None
+        self.k_scale = self.v_scale = None
+        if w.kv_format == "bf16":
+            self.k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+            self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+            kd, vd = dev_bf16(w.k), dev_bf16(w.v)
+            kds = vds = None
+        elif w.kv_format == "int8":
+            self.k_pool = torch.zeros(shape, dtype=torch.int8, device=DEV)
+            self.v_pool = torch.zeros(shape, dtype=torch.int8, device=DEV)
+            self.k_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+            self.v_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+            kd, vd = dev(w.k), dev(w.v)
+            kds, vds = dev(w.k_scales), dev(w.v_scales)
+        elif w.kv_format == "fp8":
+            self.k_pool = torch.full(shape, synth.FP8_NAN, dtype=torch.uint8, device=DEV)
+            self.v_pool = torch.full(shape, synth.FP8_NAN, dtype=torch.uint8, device=DEV)
+            kd, vd = dev(w.k), dev(w.v)
+            kds = vds = None
+            self.k_scale = torch.tensor([float(w.k_scale)], dtype=torch.float32, device=DEV)
+            self.v_scale = torch.tensor([float(w.v_scale)], dtype=torch.float32, device=DEV)
+        else:
+            raise ValueError(w.kv_format)
+        for bt in self.tables:
+            wp = w.with_block_table(bt)
+            synth.fill_pool(wp, self.k_pool, kd, self.k_scales, kds)
+            synth.fill_pool(wp, self.v_pool, vd, self.v_scales, vds)
+        del kd, vd, kds, vds
+        self.bts = [dev(t) for t in self.tables]
+
+    def paged(self, which: int = 0, causal=None) -> ops.Paged:
+        w = self.w
+        return ops.Paged(self.bts[which], self.cu_q, self.ctx, int(w.q_lens.max()),
+                         int(w.ctx_lens.max()), w.block_size, w.num_blocks, w.num_q_heads,
+                         w.num_kv_heads, w.head_dim, w.softmax_scale,
+                         w.causal if causal is None else causal)
+
+    def out(self, dtype=torch.float32) -> torch.Tensor:
+        w = self.w
+        return torch.full((int(w.q_lens.sum()), w.num_q_heads, w.head_dim), float("nan"),
+                          dtype=dtype, device=DEV)
+
+    # ---------------------------------------------------------------- arms
+    def run_bf16(self, which=0, out_dtype=torch.float32):
+        o = self.out(out_dtype)
+        ops.pa_prefill_bf16(self.paged(which), self.q, self.k_pool, self.v_pool, o)
+        return o
+
+    def run_int8kv(self, which=0, out_dtype=torch.float32):
+        o = self.out(out_dtype)
+        ops.pa_prefill_int8kv(self.paged(which), self.q, self.k_pool, self.v_pool, self.k_scales,
+                              self.v_scales, o)
+        return o
+
+    def run_k_passes(self, which=0):
+        w = self.w
+        total = int(w.ctx_lens.sum())
+        ks = torch.full((total, w.num_kv_heads), float("nan"), dtype=torch.float32, device=DEV)
+        k8 = torch.full((total, w.num_kv_heads, w.head_dim), 99, dtype=torch.int8, device=DEV)
+        p = self.paged(which)
+        ops.pa_k_stats(p, self.k_pool, self.k_scales, self.cu_ctx, ks)
+        ops.pa_k_quant(p, self.k_pool, self.k_scales, self.cu_ctx, ks, k8)
+        return ks, k8
+
+    def run_int8qk(self, which=0, out_dtype=torch.float32):
+        ks, k8 = self.run_k_passes(which)
+        o = self.out(out_dtype)
+        ops.pa_prefill_int8qk(self.paged(which), self.q, k8, ks, self.cu_ctx, self.v_pool,
+                              self.v_scales, o)
+        return o, ks, k8
+
+    def run_fp8(self, max_seq=None, which=0, out_dtype=torch.float32):
+        w = self.w
+        max_seq = max_seq or int(w.ctx_lens.max())
+        shape = (w.num_reqs, max_seq, w.num_kv_heads, w.head_dim)
+        ksc = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+        vsc = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+        p = self.paged(which)
+        ops.pa_fp8_dense_dequant(p, self.k_pool, self.v_pool, self.k_scale, self.v_scale, max_seq,
+                                 ksc, vsc)
+        o = self.out(out_dtype)
+        ops.pa_prefill_bf16(ops.scratch_view(p, max_seq, DEV), self.q, ksc, vsc, o)
+        return o, ksc, vsc
+
+    def gather(self, pool, which=0):
+        w = self.w
+        dense = torch.empty((int(w.ctx_lens.sum()), w.num_kv_heads, w.head_dim), dtype=pool.dtype,
+                            device=DEV)
+        ops.pa_gather_kv(self.paged(which), pool, self.cu_ctx, dense)
+        return dense
+
+
+def host_pools_multi(w: synth.Workload, tables, poison_all: bool):
+    """Host pools with the workload written at every placement in `tables`."""
+    pools = synth.host_pools(w.with_block_table(tables[0]), poison_all=poison_all)
+    for bt in tables[1:]:
+        wp = w.with_block_table(bt)
+        synth.fill_pool(wp, pools["k"], w.k, pools.get("k_scales"), w.k_scales)
+        synth.fill_pool(wp, pools["v"], w.v, pools.get("v_scales"), w.v_scales)
+        if not poison_all:
+            for r in range(w.num_reqs):
+                last = int(wp.blocks_of(r)[-1])
+                n = int(w.ctx_lens[r]) - (len(wp.blocks_of(r)) - 1) * w.block_size
+                pools["k"][last, n:] = w.kv_poison
+                pools["v"][last, n:] = w.kv_poison
+    return pools
+
+
+def oracle_rows(orc, w, pools, rows, block_table=None):
+    bt = w.block_table if block_table is None else block_table
+    return orc.prefill(bt, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"], w.softmax_scale,
+                       causal=w.causal, k_scales=pools.get("k_scales"),
+                       v_scales=pools.get("v_scales"), rows=rows)

@@ -1,0 +1,116 @@
+"""Host-side checks that need no GPU: the C-ABI library loads and exports
+every entry point its header declares, argument errors come back as status
+codes without touching the device, and the seeded workloads have the shapes
+and placements the pages describe."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from paged_kv_prefill_amd import ops, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_kv_prefill.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ops.ENTRY_POINTS:
+        assert n in names
+    assert set(names) == set(ops.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(ops.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert ops.build_id().startswith("paged_kv_prefill gfx950")
+    assert ops.status_string(ops.PA_ERR_SHAPE) != ops.status_string(ops.PA_OK)
+
+
+def _args(**kw):
+    a = ops.PagedArgs()
+    base = dict(block_table=16, stride_bt=4, cu_q_lens=32, ctx_lens=48, num_reqs=1, max_q_len=8,
+                max_ctx_len=16, block_size=4, num_blocks=8, num_q_heads=4, num_kv_heads=2,
+                head_dim=64, softmax_scale=0.125, causal=1, stride_block=4 * 2 * 64,
+                stride_tok=2 * 64, stride_head=64, stride_sblock=8, stride_stok=2)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+# every case below must fail validation: the library then returns before any HIP call
+BAD = [
+    (dict(block_table=None), ops.PA_ERR_NULL),
+    (dict(ctx_lens=None), ops.PA_ERR_NULL),
+    (dict(num_q_heads=3), ops.PA_ERR_SHAPE),
+    (dict(head_dim=96, stride_head=96, stride_tok=192, stride_block=768), ops.PA_ERR_UNSUPPORTED),
+    (dict(block_size=0), ops.PA_ERR_SHAPE),
+    (dict(max_q_len=32), ops.PA_ERR_SHAPE),
+    (dict(causal=2), ops.PA_ERR_SHAPE),
+    (dict(stride_tok=130), ops.PA_ERR_SHAPE),
+    (dict(max_ctx_len=2 ** 30, max_q_len=8), ops.PA_ERR_TOO_LARGE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_argument_errors_return_status(kw, code):
+    L = ops.lib()
+    a = _args(**kw)
+    p = C.c_void_p(4096)
+    rc = L.pa_prefill_bf16(C.byref(a), p, p, p, p, ops.PA_DTYPE_F32, None)
+    assert rc == code
+
+
+def test_entry_point_specific_errors():
+    L = ops.lib()
+    a = _args()
+    p = C.c_void_p(4096)
+    odd = C.c_void_p(4100)
+    assert L.pa_prefill_bf16(None, p, p, p, p, 0, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16(C.byref(a), None, p, p, p, 0, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16(C.byref(a), p, p, p, p, 7, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_prefill_bf16(C.byref(a), odd, p, p, p, 0, None) == ops.PA_ERR_SHAPE
+    assert L.pa_prefill_int8kv(C.byref(a), p, p, p, None, p, p, 0, None) == ops.PA_ERR_NULL
+    assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_F32, None, p, p, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_INT8, None, p, p, None) == ops.PA_ERR_NULL
+    assert L.pa_k_quant(C.byref(a), p, ops.PA_DTYPE_BF16, None, p, p, None, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_int8qk(C.byref(a), p, p, p, p, p, ops.PA_DTYPE_FP8_E4M3, None, p, 0,
+                               None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_fp8_dense_dequant(C.byref(a), p, p, p, p, 8, p, p, None) == ops.PA_ERR_SHAPE
+    assert L.pa_fp8_dense_dequant(C.byref(a), p, p, None, p, 16, p, p, None) == ops.PA_ERR_NULL
+    assert L.pa_gather_kv(C.byref(a), p, 4, p, p, None) == ops.PA_ERR_UNSUPPORTED
+
+
+def test_pool_geometry_matches_pages():
+    """Block stride 880 * 4 * 256 = 901,120 elements; the int32 product
+    overflows from block 2,384 on, so ids above 2,383 are the unsafe ones; the
+    top placement of the 2,600-block pool clears that by 217 blocks (HyperQwen
+    PR #91, blocking review)."""
+    w = synth.config_bigpool_bf16()
+    assert w.stride_block == 901_120
+    assert 2383 * w.stride_block < 2 ** 31 <= 2384 * w.stride_block
+    top = w.extra["top_block_table"]
+    assert top.shape == (1, 23) and int(top.min()) == 2577 and int(top.max()) == 2599
+    assert w.num_blocks - 2383 == 217
+    assert w.block_table.tolist() == [list(range(23))]
+    assert int(w.ctx_lens[0]) - 22 * 880 == 640          # valid slots in the last block
+
+
+def test_workload_recipes():
+    assert synth.config_tiny().block_table.tolist() == [[2, 4, 3]]
+    b = synth.config_batched(lite=True)
+    assert b.ctx_lens.tolist() == [35237, 44552, 41900, 25987, 44439, 45979, 45723, 7476]
+    assert b.num_blocks * b.stride_block > 2 ** 32
+    used = np.concatenate([b.blocks_of(r) for r in range(b.num_reqs)])
+    assert len(used) == len(set(used.tolist())) == 335
+    assert np.mean(used > 2383) > 0.6 and int(used.max()) < 8000

@@ -336,3 +336,61 @@ def test_fp8_dense_dequant_matches_torch_casts(orc, pow2):
         assert np.all(got[0, 50:] == 0)
         if pow2:  # exact: every e4m3fn value times a power of two is a bf16 value
             assert np.array_equal(dec_bf16(got[0, :50]), dec.double().numpy() * float(scale))
+
+
+# ------------------------------------------------------------------ int8-QK arm
+def _quant_exact_rows(rng, shape, step):
+    """bf16 rows n * step with integers |n| <= 127 and one |n| = 127 per row,
+    so that the per-row absmax/127 quantisation reproduces n exactly."""
+    n = rng.integers(-126, 127, size=shape).astype(np.int32)
+    pick = rng.integers(0, shape[-1], size=shape[:-1])
+    sign = np.where(rng.integers(0, 2, size=shape[:-1]) == 0, -127, 127)
+    np.put_along_axis(n, pick[..., None], sign[..., None], axis=-1)
+    return n, synth.f32_to_bf16_bits(n.astype(np.float32) * np.float32(step))
+
+
+@pytest.mark.parametrize("d,group,causal", [(64, 2, True), (256, 4, True), (128, 1, False)])
+def test_int8qk_arm_is_exact_on_quantisation_exact_inputs(orc, d, group, causal):
+    """When every q and k row is an integer multiple of a power-of-two step with
+    absmax 127 steps, quantisation loses nothing: the arm's codes are those
+    integers, its scales are the steps, and its output is exact attention."""
+    rng = np.random.default_rng(40 + d)
+    w = synth.make_case(41, [6, 3], [23, 9], 5, 2 * group, 2, d, causal=causal)
+    nq, w.q = _quant_exact_rows(rng, w.q.shape, 2.0 ** -5)
+    nk, w.k = _quant_exact_rows(rng, w.k.shape, 2.0 ** -6)
+    pools = synth.host_pools(w)
+    ks = orc.k_stats(w.block_table, w.ctx_lens, pools["k"])
+    k8 = orc.k_quant(w.block_table, w.ctx_lens, pools["k"], ks)
+    assert np.all(ks == np.float32(2.0 ** -6)) and np.array_equal(k8, nk.astype(np.int8))
+    emu = orc.prefill_int8qk(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, k8, ks, pools["v"],
+                             w.softmax_scale, causal=causal)
+    ref = sdpa_reference(w, causal=causal)
+    assert np.max(np.abs(emu - ref)) < 1e-12
+
+
+def test_int8qk_arm_quantisation_error_is_bounded(orc):
+    """On generic data the arm differs from exact attention only through the
+    rounding of q and k to 255 levels: logit errors are bounded by
+    scale * (sum |q||dk| + |k||dq| + |dq||dk|) with |dq| <= sq/2, |dk| <= sk/2."""
+    w = synth.make_case(42, [40], [300], 16, 4, 2, 64)
+    pools = synth.host_pools(w)
+    ks = orc.k_stats(w.block_table, w.ctx_lens, pools["k"])
+    k8 = orc.k_quant(w.block_table, w.ctx_lens, pools["k"], ks)
+    emu = orc.prefill_int8qk(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, k8, ks, pools["v"],
+                             w.softmax_scale)
+    ref = run_oracle(orc, w)
+    Q, K, V = dec_bf16(w.q), dense_values(w, "k"), dense_values(w, "v")
+    sq = np.abs(Q).max(-1) / 127.0
+    skk = np.abs(K).max(-1) / 127.0
+    dmax = 0.0
+    for i in range(40):
+        for h in range(4):
+            g = h // 2
+            bound = w.softmax_scale * (np.abs(Q[i, h]).sum() * skk[:, g] / 2
+                                       + np.abs(K[:, g]).sum(-1) * sq[i, h] / 2
+                                       + 64 * sq[i, h] * skk[:, g] / 4)
+            # softmax is 1-Lipschitz per logit in the max norm up to the spread of V
+            spread = V[:, g].max(0) - V[:, g].min(0)
+            dmax = max(dmax, float(np.max(np.abs(emu[i, h] - ref[i, h]) - 2 * bound.max() * spread)))
+    assert dmax <= 0.0
+    assert 1e-4 < np.max(np.abs(emu - ref)) < 0.1
