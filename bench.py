@@ -1,0 +1,321 @@
+"""Benchmark of chunked-prefill attention over a paged KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--arms all|none] [--no-cpu]
+
+One step is one launch of the bf16 prefill attention over the headline
+workload: a 2,048-token causal chunk at a 20,000-token context, head_dim 256,
+16 q / 4 KV heads, block 880, in a 2,600-block bf16 pool (the request placed at
+the top of the pool, blocks 2,577-2,599, so every offset needs 64 bits).  The
+timed region launches K steps back to back on torch's current stream; HIP
+events on that stream time each launch.  Inputs are seeded synthetic N(0,1)
+bf16 values, resident in HBM before timing starts.
+
+Printed: one JSON line with the headline tokens/s, the roofline of the
+attention kernel (algorithmic FLOPs per launch / measured launch time against
+the bf16 dense MFMA peak), the CPU oracle's rate on a bounded sample, and the
+other arms (int8 KV exact-QK, int8-QK with its two K passes, fp8 KV through
+the dense bf16 scratch, the batched 8-request chunk) measured the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from paged_kv_prefill_amd import ops, synth  # noqa: E402
+
+METRIC = "prefill attn tokens/s (2048-tok chunk, 20k ctx, hd256) + % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+DEV = "cuda"
+
+
+# ------------------------------------------------------------------ setup helpers
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def causal_pairs(q_lens, ctx_lens) -> int:
+    """Sum over chunk rows of the number of keys each row attends to."""
+    tot = 0
+    for lq, L in zip(q_lens, ctx_lens):
+        lq, L = int(lq), int(L)
+        tot += (L - lq + 1 + L) * lq // 2
+    return tot
+
+
+def attn_flops(w, q_lens=None, ctx_lens=None) -> float:
+    q_lens = w.q_lens if q_lens is None else q_lens
+    ctx_lens = w.ctx_lens if ctx_lens is None else ctx_lens
+    return 4.0 * w.head_dim * w.num_q_heads * causal_pairs(q_lens, ctx_lens)
+
+
+class Pools:
+    """A workload's pools in HBM (poisoned outside the request), its Q, metadata."""
+
+    def __init__(self, w, block_table):
+        self.w = w
+        shape = w.pool_shape
+        self.bt = dev(block_table)
+        self.cu_q = dev(w.cu_q_lens)
+        self.ctx = dev(w.ctx_lens)
+        self.cu_ctx = dev(w.cu_ctx_lens)
+        self.q = dev_bf16(w.q)
+        self.k_scales = self.v_scales = None
+        wp = w.with_block_table(block_table)
+        if w.kv_format == "bf16":
+            self.k = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+            self.v = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+            synth.fill_pool(wp, self.k, dev_bf16(w.k))
+            synth.fill_pool(wp, self.v, dev_bf16(w.v))
+        elif w.kv_format == "int8":
+            self.k = torch.zeros(shape, dtype=torch.int8, device=DEV)
+            self.v = torch.zeros(shape, dtype=torch.int8, device=DEV)
+            self.k_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+            self.v_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+            synth.fill_pool(wp, self.k, dev(w.k), self.k_scales, dev(w.k_scales))
+            synth.fill_pool(wp, self.v, dev(w.v), self.v_scales, dev(w.v_scales))
+        else:
+            self.k = torch.full(shape, synth.FP8_NAN, dtype=torch.uint8, device=DEV)
+            self.v = torch.full(shape, synth.FP8_NAN, dtype=torch.uint8, device=DEV)
+            synth.fill_pool(wp, self.k, dev(w.k))
+            synth.fill_pool(wp, self.v, dev(w.v))
+            self.k_scale = torch.tensor([float(w.k_scale)], dtype=torch.float32, device=DEV)
+            self.v_scale = torch.tensor([float(w.v_scale)], dtype=torch.float32, device=DEV)
+
+    def paged(self, cu_q=None, ctx=None, max_q=None, max_ctx=None):
+        w = self.w
+        return ops.Paged(self.bt, self.cu_q if cu_q is None else cu_q,
+                         self.ctx if ctx is None else ctx,
+                         int(w.q_lens.max()) if max_q is None else max_q,
+                         int(w.ctx_lens.max()) if max_ctx is None else max_ctx,
+                         w.block_size, w.num_blocks, w.num_q_heads, w.num_kv_heads,
+                         w.head_dim, w.softmax_scale, w.causal)
+
+    def out(self, rows=None):
+        w = self.w
+        rows = int(w.q_lens.sum()) if rows is None else rows
+        return torch.empty((rows, w.num_q_heads, w.head_dim), dtype=torch.float32, device=DEV)
+
+
+def time_launches(fns, steps: int, warmup: int):
+    """Run the launch sequence `fns` warmup + steps times; HIP events on the
+    current stream bracket each function.  Returns (per-function mean ms over
+    the timed steps, wall ms per step)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in fns] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            ev[s][i][0].record(stream)
+            f()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+           for i in range(len(fns))]
+    return per, wall
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, block_table, target_s: float = 12.0):
+    """The oracle as it stands, on the host cores, over a sample of chunk rows
+    (all q heads) spread over the chunk; tokens/s of the sample."""
+    from oracle import oracle as orc
+    pools = synth.host_pools(w.with_block_table(block_table), poison_all=False)
+    threads = len(os.sched_getaffinity(0))
+    lib = orc.load()
+    n = 8
+    while True:
+        rows = np.linspace(0, int(w.q_lens[0]) - 1, n).astype(np.int32)
+        t0 = time.perf_counter()
+        orc.prefill(block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
+                    w.softmax_scale, rows=rows, threads=threads, lib=lib)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or n >= int(w.q_lens[0]):
+            break
+        n = min(int(w.q_lens[0]), max(n * 2, int(n * target_s / max(dt, 1e-3))))
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of the 2,048 chunk rows (all 16 q heads, ~20k keys each), "
+                      f"fp64 oracle, {dt:.1f} s wall"}
+
+
+# ------------------------------------------------------------------ arms
+def arm_bigpool_bf16(steps, warmup):
+    w = synth.config_bigpool_bf16()
+    top = w.extra["top_block_table"]
+    P = Pools(w, top)
+    p = P.paged()
+    out = P.out()
+    ws = ops.workspace(p, ops.PA_ENTRY_PREFILL_BF16)
+    fn = lambda: ops.pa_prefill_bf16(p, P.q, P.k, P.v, out, ws)
+    (ms,), wall = time_launches([fn], steps, warmup)
+    assert torch.isfinite(out).all().item()
+    return w, top, ms, wall, attn_flops(w)
+
+
+def arm_int8(steps, warmup):
+    w = synth.config_bigpool_int8()
+    P = Pools(w, w.extra["top_block_table"])
+    p = P.paged()
+    out = P.out()
+    total = int(w.ctx_lens.sum())
+    ks = torch.empty((total, w.num_kv_heads), dtype=torch.float32, device=DEV)
+    k8 = torch.empty((total, w.num_kv_heads, w.head_dim), dtype=torch.int8, device=DEV)
+    ws_e = ops.workspace(p, ops.PA_ENTRY_PREFILL_INT8KV)
+    ws_q = ops.workspace(p, ops.PA_ENTRY_PREFILL_INT8QK)
+    exact = lambda: ops.pa_prefill_int8kv(p, P.q, P.k, P.v, P.k_scales, P.v_scales, out, ws_e)
+    stats = lambda: ops.pa_k_stats(p, P.k, P.k_scales, P.cu_ctx, ks)
+    quant = lambda: ops.pa_k_quant(p, P.k, P.k_scales, P.cu_ctx, ks, k8)
+    qk8 = lambda: ops.pa_prefill_int8qk(p, P.q, k8, ks, P.cu_ctx, P.v, P.v_scales, out, ws_q)
+    (t_exact,), _ = time_launches([exact], steps, warmup)
+    (t_stats, t_quant, t_qk8), _ = time_launches([stats, quant, qk8], steps, warmup)
+    fl = attn_flops(w)
+    elems = total * w.num_kv_heads * w.head_dim
+    rows = total * w.num_kv_heads
+    stats_bytes = elems + rows * 4 + rows * 4
+    quant_bytes = elems + rows * 4 + rows * 4 + elems
+    blended = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
+    chunk = int(w.q_lens.sum())
+    return {
+        "int8kv_exact_qk": {"ms": t_exact, "tokens_per_s": chunk / t_exact * 1e3,
+                            "tflops": fl / t_exact * 1e-9,
+                            "mfma_frac": fl / t_exact * 1e-9 / PEAK_BF16_TFLOPS},
+        "int8_qk": {"ms_total": t_stats + t_quant + t_qk8, "ms_attention": t_qk8,
+                    "tokens_per_s": chunk / (t_stats + t_quant + t_qk8) * 1e3,
+                    "attention_tops": fl / t_qk8 * 1e-9,
+                    "mfma_frac_blended_peak": fl / t_qk8 * 1e-9 / blended,
+                    "k_stats": {"ms": t_stats, "gbs": stats_bytes / t_stats * 1e-6,
+                                "hbm_frac": stats_bytes / t_stats * 1e-6 / PEAK_HBM_GBS},
+                    "k_quant": {"ms": t_quant, "gbs": quant_bytes / t_quant * 1e-6,
+                                "hbm_frac": quant_bytes / t_quant * 1e-6 / PEAK_HBM_GBS}},
+    }
+
+
+def arm_fp8(steps, warmup):
+    w, chunks = synth.config_fp8_32k()
+    P = Pools(w, w.block_table)
+    max_seq = synth.FP8_CTX
+    shape = (1, max_seq, w.num_kv_heads, w.head_dim)
+    ksc = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    vsc = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+    cu_q = dev(np.array([0, synth.CHUNK], np.int32))
+    fns, flops, dq_bytes = [], 0.0, 0
+    outs = [P.out(synth.CHUNK) for _ in chunks]
+    ws = None
+    for c, (q0, L) in enumerate(chunks):
+        ctx = dev(np.array([L], np.int32))
+        p = P.paged(cu_q=cu_q, ctx=ctx, max_q=synth.CHUNK, max_ctx=L)
+        ps = ops.scratch_view(p, max_seq, DEV)
+        if ws is None:   # sized for the longest call
+            wp = P.paged(cu_q=cu_q, ctx=dev(np.array([max_seq], np.int32)), max_q=synth.CHUNK,
+                         max_ctx=max_seq)
+            ws = ops.workspace(ops.scratch_view(wp, max_seq, DEV), ops.PA_ENTRY_PREFILL_BF16)
+        q = P.q[q0:q0 + synth.CHUNK]
+        fns.append(lambda p=p: ops.pa_fp8_dense_dequant(p, P.k, P.v, P.k_scale, P.v_scale,
+                                                        max_seq, ksc, vsc))
+        fns.append(lambda ps=ps, q=q, o=outs[c]: ops.pa_prefill_bf16(ps, q, ksc, vsc, o, ws))
+        flops += attn_flops(w, [synth.CHUNK], [L])
+        dq_bytes += 2 * L * w.num_kv_heads * w.head_dim * 3
+    per, wall = time_launches(fns, max(2, steps // 4), 1)
+    t_dq = sum(per[0::2])
+    t_at = sum(per[1::2])
+    return {"fp8_32k_16_chunks": {
+        "ms_total": t_dq + t_at, "ms_dequant": t_dq, "ms_attention": t_at,
+        "tokens_per_s": synth.FP8_CTX / (t_dq + t_at) * 1e3,
+        "attention_mfma_frac": flops / t_at * 1e-9 / PEAK_BF16_TFLOPS,
+        "dequant_gbs": dq_bytes / t_dq * 1e-6,
+        "dequant_hbm_frac": dq_bytes / t_dq * 1e-6 / PEAK_HBM_GBS}}
+
+
+def arm_batched(steps, warmup):
+    w = synth.config_batched()
+    P = Pools(w, w.block_table)
+    p = P.paged()
+    out = P.out()
+    ws = ops.workspace(p, ops.PA_ENTRY_PREFILL_BF16)
+    fn = lambda: ops.pa_prefill_bf16(p, P.q, P.k, P.v, out, ws)
+    (ms,), _ = time_launches([fn], max(3, steps // 2), warmup)
+    fl = attn_flops(w)
+    return {"batched_8x2048": {"ms": ms, "tokens_per_s": int(w.q_lens.sum()) / ms * 1e3,
+                               "tflops": fl / ms * 1e-9,
+                               "mfma_frac": fl / ms * 1e-9 / PEAK_BF16_TFLOPS}}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--arms", default="all", choices=["all", "none"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ops.lib()   # fail loudly when the HIP library is not built
+
+    w, top, ms, wall, flops = arm_bigpool_bf16(args.steps, args.warmup)
+    chunk = int(w.q_lens.sum())
+    achieved = flops / ms * 1e-9                     # TFLOP/s
+    line = {
+        "metric": METRIC,
+        "value": chunk / (wall * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bigpool_bf16: 1 request, 2,048-token causal chunk at 20,000 "
+                               "context, 16 q / 4 KV heads, head_dim 256, block 880, "
+                               "2,600-block pool, request on blocks 2,577-2,599",
+                   "global_batch": chunk, "seq_len": int(w.ctx_lens[0]), "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel_ms": ms, "flops_per_launch": flops},
+        "library": ops.build_id(),
+    }
+    if args.arms == "all":
+        arms = {}
+        arms.update(arm_int8(args.steps, args.warmup))
+        torch.cuda.empty_cache()
+        arms.update(arm_fp8(args.steps, args.warmup))
+        torch.cuda.empty_cache()
+        arms.update(arm_batched(args.steps, args.warmup))
+        line["arms"] = arms
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, top)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,8 +26,16 @@
  *     pa_paged_args struct itself is read on the host during the call only.
  *   - Every call is asynchronous on `stream`; nothing synchronises the host.
  *   - The library allocates nothing and keeps no state between calls: all
- *     buffers (outputs, the fp8 scratch, k8/ks intermediates) belong to the
- *     caller and must stay alive until the stream work that uses them is done.
+ *     buffers (outputs, the fp8 scratch, k8/ks intermediates, the attention
+ *     workspace) belong to the caller and must stay alive until the stream work
+ *     that uses them is done.
+ *   - The attention entry points take a device workspace of at least
+ *     pa_workspace_bytes(args, entry) bytes (16-byte aligned).  Each call first
+ *     lays the request's V (and, for pa_prefill_int8kv, K) out once as per-tile
+ *     images in the kernel's LDS layout (64 keys per tile: a transposed fp16 V
+ *     tile, or a bf16 code K tile, plus 64 fp32 per-key scales), then runs the
+ *     attention, both on `stream`.  Calls that overlap on the same workspace
+ *     race.
  *   - Return value: PA_OK (0), or a negative PA_ERR_* code.  On an argument
  *     error nothing is enqueued.  PA_ERR_LAUNCH means the launch itself failed
  *     (hipGetLastError after the launch).  No C++ exception crosses the ABI.
@@ -41,6 +49,7 @@
 #ifndef PAGED_KV_PREFILL_H
 #define PAGED_KV_PREFILL_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -55,6 +64,12 @@ extern "C" {
 #define PA_ERR_UNSUPPORTED -3   /* head_dim or dtype outside what is built        */
 #define PA_ERR_LAUNCH      -4   /* the kernel launch failed                       */
 #define PA_ERR_TOO_LARGE   -5   /* a size exceeds a documented maximum            */
+#define PA_ERR_WORKSPACE   -6   /* workspace smaller than pa_workspace_bytes()    */
+
+/* attention entry points, for pa_workspace_bytes */
+#define PA_ENTRY_PREFILL_BF16    1
+#define PA_ENTRY_PREFILL_INT8KV  2
+#define PA_ENTRY_PREFILL_INT8QK  3
 
 /* element types */
 #define PA_DTYPE_F32        0
@@ -76,7 +91,7 @@ typedef struct pa_paged_args {
     int32_t num_q_heads;          /* multiple of num_kv_heads                              */
     int32_t num_kv_heads;
     int32_t head_dim;             /* 64, 128 or 256                                        */
-    float softmax_scale;          /* logit scale, e.g. 1/sqrt(head_dim)                    */
+    float softmax_scale;          /* logit scale > 0, e.g. 1/sqrt(head_dim)                */
     int32_t causal;               /* 1: bottom-right causal; 0: every row sees all L keys  */
     int64_t stride_block;         /* KV pool strides in elements                           */
     int64_t stride_tok;
@@ -97,7 +112,8 @@ typedef struct pa_paged_args {
  * stay below 65520 in magnitude (fp16 range); larger ones give inf/NaN rows.
  */
 int pa_prefill_bf16(const pa_paged_args *args, const void *q, const void *k_pool,
-                    const void *v_pool, void *out, int32_t out_dtype, hipStream_t stream);
+                    const void *v_pool, void *out, int32_t out_dtype, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_prefill_int8kv -- the exact-QK arm over an int8 per-token-head pool
@@ -110,7 +126,8 @@ int pa_prefill_bf16(const pa_paged_args *args, const void *q, const void *k_pool
  */
 int pa_prefill_int8kv(const pa_paged_args *args, const void *q, const int8_t *k_pool,
                       const int8_t *v_pool, const float *k_scales, const float *v_scales,
-                      void *out, int32_t out_dtype, hipStream_t stream);
+                      void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /*
  * pa_k_stats -- first pass of the int8-QK prefill (HyperQwen PR #109: the
@@ -146,7 +163,15 @@ int pa_k_quant(const pa_paged_args *args, const void *k_pool, int32_t k_dtype,
 int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8,
                       const float *ks, const int32_t *cu_ctx, const void *v_pool,
                       int32_t v_dtype, const float *v_scales, void *out, int32_t out_dtype,
-                      hipStream_t stream);
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_workspace_bytes -- device workspace an attention entry point needs for
+ * these arguments: num_reqs * ceil(max_ctx_len / 64) * num_kv_heads tile images
+ * of 128 * head_dim + 256 bytes (twice that for PA_ENTRY_PREFILL_INT8KV).
+ * Returns 0 for invalid arguments or an unknown entry.
+ */
+size_t pa_workspace_bytes(const pa_paged_args *args, int32_t entry);
 
 /*
  * pa_fp8_dense_dequant -- one-time dense dequant of an fp8 paged pool

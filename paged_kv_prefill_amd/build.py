@@ -19,12 +19,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_kv_prefill.so")
-SOURCES = ["pa_attention.hip", "pa_passes.hip", "pa_api.cpp"]
-HEADERS = ["pa_device.h", "pa_kernels.h"]
+SOURCES = ["pa_attention.hip", "pa_images.hip", "pa_passes.hip", "pa_api.cpp"]
+HEADERS = ["pa_device.h", "pa_kernels.h", "pa_layout.h"]
 PUBLIC_HEADER = os.path.join(ROOT, "include", "paged_kv_prefill.h")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # the ILP-first machine scheduler issues LDS operand reads ahead of the
+         # MFMAs that consume them (the default one serialises read -> wait -> MFMA)
+         "-mllvm", "--amdgpu-sched-strategy=iterative-ilp",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 

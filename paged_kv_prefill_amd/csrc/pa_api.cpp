@@ -3,9 +3,11 @@
 #include "../../include/paged_kv_prefill.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "pa_kernels.h"
+#include "pa_layout.h"
 
 #ifndef PA_BUILD_ID
 #define PA_BUILD_ID "unversioned"
@@ -36,6 +38,7 @@ int check_common(const pa_paged_args *a, int elem_bytes, bool needs_q) {
     if (a->max_ctx_len < 0 || a->max_q_len < 0 || (needs_q && a->max_q_len > a->max_ctx_len))
         return PA_ERR_SHAPE;
     if (a->causal != 0 && a->causal != 1) return PA_ERR_SHAPE;
+    if (!(a->softmax_scale > 0.0f) || a->softmax_scale == INFINITY) return PA_ERR_SHAPE;
     if (a->stride_block < 1 || a->stride_tok < 1 || a->stride_head < 1) return PA_ERR_SHAPE;
     // rows are read as 16-byte vectors: every row start must be 16-byte aligned
     const int64_t q16 = 16 / elem_bytes;
@@ -105,21 +108,68 @@ int check_scales(const pa_paged_args *a, const float *s) {
 
 int launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+int64_t image_count(const pa_paged_args *a) {
+    return (int64_t)a->num_reqs * tiles_per_request(a->max_ctx_len) * a->num_kv_heads;
+}
+
+// bytes of workspace an attention entry point needs: V^T tile images, plus K
+// tile images for the int8-KV exact arm
+int64_t workspace_need(const pa_paged_args *a, int32_t entry) {
+    const int64_t n = image_count(a) * image_bytes(a->head_dim);
+    return entry == PA_ENTRY_PREFILL_INT8KV ? 2 * n : n;
+}
+
+int check_workspace(const pa_paged_args *a, int32_t entry, void *ws, size_t bytes) {
+    if (!ws) return PA_ERR_NULL;
+    if (!aligned16(ws)) return PA_ERR_SHAPE;
+    if ((int64_t)bytes < workspace_need(a, entry)) return PA_ERR_WORKSPACE;
+    return PA_OK;
+}
+
+ImageParams image_params(const pa_paged_args *a, void *ws) {
+    ImageParams p{};
+    p.bt = a->block_table;
+    p.stride_bt = a->stride_bt;
+    p.ctx_lens = a->ctx_lens;
+    p.num_reqs = a->num_reqs;
+    p.Hkv = a->num_kv_heads;
+    p.D = a->head_dim;
+    p.block_size = a->block_size;
+    p.max_ctx = a->max_ctx_len;
+    p.bsdiv = make_fastdiv((uint32_t)a->block_size);
+    p.num_blocks = a->num_blocks;
+    p.stride_block = a->stride_block;
+    p.stride_tok = a->stride_tok;
+    p.stride_head = a->stride_head;
+    p.stride_sblock = a->stride_sblock;
+    p.stride_stok = a->stride_stok;
+    p.tiles = tiles_per_request(a->max_ctx_len);
+    p.dst = ws;
+    p.dst2 = (char *)ws + image_count(a) * image_bytes(a->head_dim);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
 
 int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
-                    void *out, int32_t out_dtype, hipStream_t stream) {
+                    void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
     int rc = check_common(a, 2, true);
     if (rc) return rc;
     if ((rc = check_out(q, out, out_dtype))) return rc;
     if (!k_pool || !v_pool) return PA_ERR_NULL;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    if ((rc = check_workspace(a, PA_ENTRY_PREFILL_BF16, workspace, workspace_bytes))) return rc;
+    ImageParams ip = image_params(a, workspace);
+    ip.src = v_pool;
+    if ((rc = launched(launch_images(ip, false, false, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.q = q;
     p.k = k_pool;
-    p.v = v_pool;
+    p.v_img = (const char *)workspace;
+    p.img_tiles = ip.tiles;
     p.out = out;
     return launched(launch_attention(KIND_BF16, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
                                      a->max_q_len, stream));
@@ -127,19 +177,26 @@ int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, c
 
 int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
                       const int8_t *v_pool, const float *k_scales, const float *v_scales,
-                      void *out, int32_t out_dtype, hipStream_t stream) {
+                      void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
     int rc = check_common(a, 1, true);
     if (rc) return rc;
     if ((rc = check_out(q, out, out_dtype))) return rc;
     if (!k_pool || !v_pool) return PA_ERR_NULL;
     if ((rc = check_scales(a, k_scales)) || (rc = check_scales(a, v_scales))) return rc;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    if ((rc = check_workspace(a, PA_ENTRY_PREFILL_INT8KV, workspace, workspace_bytes))) return rc;
+    ImageParams ip = image_params(a, workspace);
+    ip.src = v_pool;
+    ip.src_scales = v_scales;
+    ip.src2 = k_pool;
+    ip.src2_scales = k_scales;
+    if ((rc = launched(launch_images(ip, true, true, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.q = q;
-    p.k = k_pool;
-    p.v = v_pool;
-    p.kscale = k_scales;
-    p.vscale = v_scales;
+    p.v_img = (const char *)ip.dst;
+    p.k_img = (const char *)ip.dst2;
+    p.img_tiles = ip.tiles;
     p.out = out;
     return launched(launch_attention(KIND_I8KV, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
                                      a->max_q_len, stream));
@@ -183,25 +240,39 @@ int pa_k_quant(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
 
 int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, const float *ks,
                       const int32_t *cu_ctx, const void *v_pool, int32_t v_dtype,
-                      const float *v_scales, void *out, int32_t out_dtype, hipStream_t stream) {
+                      const float *v_scales, void *out, int32_t out_dtype, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
     if (v_dtype != PA_DTYPE_BF16 && v_dtype != PA_DTYPE_INT8) return PA_ERR_UNSUPPORTED;
     int rc = check_common(a, v_dtype == PA_DTYPE_INT8 ? 1 : 2, true);
     if (rc) return rc;
     if ((rc = check_out(q, out, out_dtype))) return rc;
     if (!k8 || !ks || !cu_ctx || !v_pool) return PA_ERR_NULL;
     if (v_dtype == PA_DTYPE_INT8 && (rc = check_scales(a, v_scales))) return rc;
-    if (!aligned16(k8) || !aligned16(ks) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    if (!aligned16(k8) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    if ((rc = check_workspace(a, PA_ENTRY_PREFILL_INT8QK, workspace, workspace_bytes))) return rc;
+    ImageParams ip = image_params(a, workspace);
+    ip.src = v_pool;
+    ip.src_scales = v_scales;
+    if ((rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8, false, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.cu_ctx = cu_ctx;
     p.q = q;
     p.k = k8;
     p.kscale = ks;
-    p.v = v_pool;
-    p.vscale = v_scales;
+    p.v_img = (const char *)workspace;
+    p.img_tiles = ip.tiles;
     p.out = out;
     const int kind = v_dtype == PA_DTYPE_INT8 ? KIND_QK8_VI8 : KIND_QK8_VBF16;
     return launched(launch_attention(kind, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
                                      a->max_q_len, stream));
+}
+
+size_t pa_workspace_bytes(const pa_paged_args *a, int32_t entry) {
+    if (entry != PA_ENTRY_PREFILL_BF16 && entry != PA_ENTRY_PREFILL_INT8KV &&
+        entry != PA_ENTRY_PREFILL_INT8QK)
+        return 0;
+    if (check_common(a, 1, false) != PA_OK) return 0;
+    return (size_t)workspace_need(a, entry);
 }
 
 int pa_fp8_dense_dequant(const pa_paged_args *a, const uint8_t *k_pool, const uint8_t *v_pool,
@@ -247,6 +318,7 @@ const char *pa_status_string(int32_t status) {
         case PA_ERR_UNSUPPORTED: return "head_dim or dtype not supported";
         case PA_ERR_LAUNCH: return "kernel launch failed";
         case PA_ERR_TOO_LARGE: return "size above the supported maximum";
+        case PA_ERR_WORKSPACE: return "workspace smaller than pa_workspace_bytes()";
         default: return "unknown status";
     }
 }

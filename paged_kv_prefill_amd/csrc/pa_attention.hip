@@ -9,27 +9,34 @@
 // Work decomposition.  A workgroup of 4 waves owns 128 "columns" of one
 // (request, KV head): a column is a (chunk token, q head of that KV head's
 // group) pair, so the q heads that share a KV head share every K/V tile (GQA).
-// Each wave owns 32 columns.  The KV context is streamed in tiles of 64 keys,
-// gathered from the paged pool with coalesced 16-byte loads, staged in LDS
-// (double-buffered, one barrier per tile) and consumed by MFMA.
+// Each wave owns 32 columns.  The KV context is streamed in tiles of 64 keys.
+// Workgroups of one (request, KV head) are mapped to one XCD, in order, so the
+// tiles they stream at the same time are shared through that XCD's L2.
 //
 // Transposed formulation.  The wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = the wave's
 // 32 query columns held in registers for the whole loop), then O^T = V^T P^T
 // (A = 32 dims x 16 keys of V^T from LDS, B = P^T straight from the S
-// accumulators) with v_mfma_f32_32x32x16_f16: P lies in [0, 1], where fp16
+// accumulators) with v_mfma_f32_32x32x16_f16: P lies in [0, 2^8], where fp16
 // keeps 11 significant bits against bf16's 8, and every bf16 V value of
 // magnitude below 65520 converts to fp16 exactly, so rounding P for the
 // matrix core costs 8x less accuracy than a bf16 P would.  (V of magnitude
 // 65520 or more overflows fp16 and shows as inf/NaN in the output.)
 // In the 32x32 accumulator layout lane l holds column l % 32, so every lane
-// owns one query column: the online softmax is lane-local except
-// for one exchange with the lane 32 away (v_permlane32_swap) per tile, the
-// O rescale is lane-local, and P never leaves registers.  V is transposed on
-// its way into LDS, with the keys of each 16-key group stored in the order in
-// which the S accumulator hands them to the PV MFMA, so each PV operand is one
-// 16-byte LDS read.  Both LDS tiles are XOR-swizzled by 16-byte chunk so that
-// the per-lane operand reads are bank-conflict free.
+// owns one query column: the online softmax is lane-local except for one
+// exchange with the lane 32 away (v_permlane32_swap) per tile, and P never
+// leaves registers.
+//
+// Data movement.  Tiles are double-buffered in LDS and move with gfx950's
+// direct global-to-LDS copies (global_load_lds_dwordx4, 1 KB per wave
+// instruction, no registers): K straight from the paged pool (each lane
+// fetches the chunk that the layout's XOR swizzle puts under it; the block
+// table row is cached in LDS, and with block_size >= 64 a tile spans at most
+// two blocks, so the block bases are wave-uniform scalars), V from the per-tile
+// V^T images that pa_images.hip builds once per call.  The copies of tile t+1
+// are issued before the MFMAs of tile t; one barrier per tile.  The running
+// maximum is updated lazily: O and the row sum are rescaled only when some
+// column's maximum grows by more than 2^8 (log2 units).
 //
 // The int8-QK arm replaces the QK MFMA with v_mfma_i32_32x32x32_i8 on the
 // int8 K written by the K-quant pass and on Q quantised per (token, head) in
@@ -42,74 +49,56 @@
 // value is ever rounded.
 #include "pa_device.h"
 #include "pa_kernels.h"
+#include "pa_layout.h"
 
 namespace pa {
 
-constexpr int BN = 64;           // keys per tile
+constexpr int BN = TILE_KEYS;    // keys per tile
 constexpr int NWAVE = 4;
 constexpr int NTHR = 64 * NWAVE;
 constexpr int NCOL = 32 * NWAVE;
+constexpr int LDS_MAX = 160 * 1024;
+constexpr float RESCALE_SLACK = 8.0f;   // lazy-rescale threshold, log2 units
 static_assert(NTHR == ATTN_THREADS && NCOL == ATTN_COLS, "launch geometry");
-
-// slot of key k (0..63 in the tile) in a row of the transposed V tile: within
-// each group of 16 keys, keys {0-3, 8-11} take slots 0-7 and {4-7, 12-15}
-// take slots 8-15, matching the key order of the S accumulator rows.
-__device__ __forceinline__ int vt_slot(int k) {
-    int k16 = k & 15;
-    return (k & ~15) | (k16 & 3) | ((k16 >> 3) << 2) | (((k16 >> 2) & 1) << 3);
-}
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-// byte offset of (d, slot) in a [D][64] fp16 V^T tile (8 chunks of 16 B per row)
-__device__ __forceinline__ int vt_off(int d, int slot) {
-    return d * (BN * 2) + ((((slot >> 3) ^ vt_swz(d)) << 4) | ((slot & 7) << 1));
-}
 
 template <int D, int KIND>
 struct AttnCfg {
     static constexpr bool QK8 = (KIND == KIND_QK8_VBF16 || KIND == KIND_QK8_VI8);
     static constexpr bool V_I8 = (KIND == KIND_I8KV || KIND == KIND_QK8_VI8);  // V codes + scales
-    static constexpr bool K_I8 = (KIND == KIND_I8KV);      // paged int8 K codes + scales
+    static constexpr bool K_I8 = (KIND == KIND_I8KV);      // K tile images of int8 codes + scales
+    static constexpr bool K_PAGED = (KIND == KIND_BF16);   // K straight from the bf16 pool
     static constexpr bool K_SCALED = K_I8 || QK8;          // logits need a per-key scale
-    static constexpr int K_BYTES = QK8 ? BN * D : BN * D * 2;  // K tile: int8 or bf16
-    static constexpr int V_BYTES = BN * D * 2;                 // V^T tile: fp16
-    static constexpr int KS_OFF = K_BYTES + V_BYTES;           // per-key K scales (64 floats)
-    static constexpr int VS_OFF = KS_OFF + (K_SCALED ? BN * 4 : 0);  // per-key V scales
-    static constexpr int STAGE = VS_OFF + (V_I8 ? BN * 4 : 0);
-    // paged loader: one unit = 4 consecutive keys x one 16-byte chunk of source row
-    static constexpr int SRC_ROW_BYTES = V_I8 ? D : 2 * D;
-    static constexpr int CPR = SRC_ROW_BYTES / 16;
-    static constexpr int UNITS = 16 * CPR;
-    static constexpr int UPT = (UNITS + NTHR - 1) / NTHR;
-    // dense int8 K loader (int8-QK): rows of D bytes
-    static constexpr int K8_CPR = D / 16;
-    static constexpr int K8_PER_THR = (BN * K8_CPR + NTHR - 1) / NTHR;
-    static constexpr int K8_SWZ = (K8_CPR < 8 ? K8_CPR : 8) - 1;   // XOR stays inside the row
+    static constexpr int K_ROW_BYTES = QK8 ? D : 2 * D;
+    static constexpr int K_BYTES = BN * K_ROW_BYTES;
+    static constexpr int V_BYTES = BN * D * 2;
+    static constexpr int KSTAGE = K_BYTES + (K_SCALED ? BN * 4 : 0);
+    static constexpr int VSTAGE = V_BYTES + (V_I8 ? BN * 4 : 0);
+    static constexpr int BT_OFF = 2 * KSTAGE + 2 * VSTAGE;
+    static constexpr int BT_CAP = K_PAGED ? ((LDS_MAX - BT_OFF) / 4 < 4096 ? (LDS_MAX - BT_OFF) / 4 : 4096) : 0;
+    static constexpr int LDS = BT_OFF + BT_CAP * 4;
+    static constexpr int KROW_CHUNKS = K_ROW_BYTES / 16;
+    static constexpr int KROWS_PER_INSTR = 64 / KROW_CHUNKS;
+    static constexpr int K_INSTR_PER_WAVE = K_BYTES / 1024 / NWAVE;
+    static constexpr int V_INSTR_PER_WAVE = V_BYTES / 1024 / NWAVE;
+    static constexpr int KSWZ = ktile_swz_mask(K_ROW_BYTES);
     static constexpr int KSTEPS = QK8 ? D / 32 : D / 16;
     static constexpr int DB = D / 32;
+    static_assert(K_INSTR_PER_WAVE >= 1 && V_INSTR_PER_WAVE >= 1, "tile too small");
+    static_assert(LDS <= LDS_MAX, "LDS budget");
 };
 
-// 64-bit element offset of key position `key` of request r, KV head g, d = 0.
-// Returns false (and offset 0) when the block id is outside the pool.
-__device__ __forceinline__ bool paged_row(const AttnParams &P, int r, int key, int g,
-                                          int64_t &off, int64_t &soff) {
-    FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
-    uint32_t bi = fdiv((uint32_t)key, fd);
-    uint32_t slot = (uint32_t)key - bi * (uint32_t)P.block_size;
-    int64_t blk = (int64_t)P.bt[(int64_t)r * P.stride_bt + bi];   // widen before any product
-    if (blk < 0 || blk >= P.num_blocks) {
-        off = 0;
-        soff = 0;
-        return false;
-    }
-    off = blk * P.stride_block + (int64_t)slot * P.stride_tok + (int64_t)g * P.stride_head;
-    soff = blk * P.stride_sblock + (int64_t)slot * P.stride_stok + g;
-    return true;
+__device__ __forceinline__ void dma16(const void *src, char *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, char *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
 }
 
-template <int D, int KIND, bool OUT_BF16>
+// FAST: block_size >= 64 (a tile spans at most two blocks), chosen on the host.
+template <int D, int KIND, bool OUT_BF16, bool FAST>
 __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     using C = AttnCfg<D, KIND>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -150,7 +139,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // ---- Q operand (B of S^T = K Q^T), resident for the whole KV loop
     bf16x8 qf[C::QK8 ? 1 : C::KSTEPS];
     i32x4 q8[C::QK8 ? C::KSTEPS : 1];
-    float lfac = P.scale_log2;   // log2-domain factor applied to the raw logit
+    float lfac = P.scale_log2;   // log2-domain factor of the raw logit
     if constexpr (!C::QK8) {
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks)
@@ -197,164 +186,134 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         lfac = sq * P.scale_log2;
     }
 
-    // ---- loader state
+    // ---- block-table row of this request, cached in LDS (paged K only)
+    int32_t *bt_lds = (int32_t *)(smem + C::BT_OFF);
+    const int64_t bt_row = (int64_t)r * P.stride_bt;
+    if constexpr (C::K_PAGED) {
+        const int n_blk = (n_keys - 1) / P.block_size + 1;
+        for (int i = tid; i < n_blk && i < C::BT_CAP; i += NTHR) bt_lds[i] = P.bt[bt_row + i];
+        __syncthreads();
+    }
+    auto bt_at = [&](int i) -> int64_t {
+        return (int64_t)(i < C::BT_CAP ? bt_lds[i] : P.bt[bt_row + i]);
+    };
+
+    const int64_t img_base = ((int64_t)r * P.img_tiles) * P.Hkv + g;   // image index of tile 0
     const int64_t k8_row0 = C::QK8 ? (int64_t)P.cu_ctx[r] : 0;
-    u32x4 kreg[C::QK8 ? C::K8_PER_THR : C::UPT][C::QK8 ? 1 : 4];
-    u32x4 vreg[C::UPT][4];
-    float kscl[C::K_I8 ? C::UPT : 1][4];
-    float vscl[C::V_I8 ? C::UPT : 1][4];
-    float ks_reg = 0.f;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    auto kstage = [&](int s) { return smem + s * C::KSTAGE; };
+    auto vstage = [&](int s) { return smem + 2 * C::KSTAGE + s * C::VSTAGE; };
 
-    auto load_tile = [&](int kt) {
+    // ---- K tile kt into LDS stage `stage`.  Wave instruction q fills bytes
+    // [q KB, q KB + 1 KB): lane l lands at chunk l % KROW_CHUNKS of row
+    // q * KROWS_PER_INSTR + l / KROW_CHUNKS, so it fetches the logical chunk the
+    // XOR swizzle maps there.  Rows past the context fetch a mapped dummy
+    // address; their logits are masked.
+    auto dma_k = [&](int kt, int stage) {
+        char *kl = kstage(stage);
         const int kbase = kt * BN;
+        const int pc = lane % C::KROW_CHUNKS;
+        if constexpr (C::K_PAGED) {
+            int64_t base0 = 0, base1 = 0;
+            int bnd = BN;
+            constexpr int64_t BAD = INT64_MIN;
+            if constexpr (FAST) {
+                FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
+                const int b0 = __builtin_amdgcn_readfirstlane((int)fdiv((uint32_t)kbase, fd));
+                const int first = b0 * P.block_size;
+                bnd = first + P.block_size - kbase;
+                const bool two = bnd < BN && kbase + bnd < n_keys;
+                const int blk0 = __builtin_amdgcn_readfirstlane((int)bt_at(b0));
+                const int blk1 = __builtin_amdgcn_readfirstlane(two ? (int)bt_at(b0 + 1) : blk0);
+                const int64_t gh = (int64_t)g * P.stride_head;
+                base0 = (blk0 >= 0 && blk0 < P.num_blocks)
+                            ? (int64_t)blk0 * P.stride_block + (int64_t)(kbase - first) * P.stride_tok + gh
+                            : BAD;
+                base1 = (blk1 >= 0 && blk1 < P.num_blocks)
+                            ? (int64_t)blk1 * P.stride_block +
+                                  (int64_t)(kbase - first - P.block_size) * P.stride_tok + gh
+                            : BAD;
+            }
 #pragma unroll
-        for (int iu = 0; iu < C::UPT; ++iu) {
-            const int u = tid + NTHR * iu;
-            const int dc = u % C::CPR, kg = u / C::CPR;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = kbase + kg * 4 + j;
-                int64_t off = 0, soff = 0;
-                const bool ok = (u < C::UNITS) && key < n_keys && paged_row(P, r, key, g, off, soff);
-                if constexpr (!C::QK8) {
-                    if constexpr (C::K_I8) {
-                        kreg[iu][j] = ok ? *(const u32x4 *)((const int8_t *)P.k + off + dc * 16) : zero4;
-                        kscl[iu][j] = ok ? P.kscale[soff] : 0.f;
-                    } else {
-                        kreg[iu][j] = ok ? *(const u32x4 *)((const __bf16 *)P.k + off + dc * 8) : zero4;
-                    }
-                }
-                if constexpr (C::V_I8) {
-                    vreg[iu][j] = ok ? *(const u32x4 *)((const int8_t *)P.v + off + dc * 16) : zero4;
-                    vscl[iu][j] = ok ? P.vscale[soff] : 0.f;
+            for (int i = 0; i < C::K_INSTR_PER_WAVE; ++i) {
+                const int q = wave * C::K_INSTR_PER_WAVE + i;
+                const int row = q * C::KROWS_PER_INSTR + lane / C::KROW_CHUNKS;
+                const int c = pc ^ (row & C::KSWZ);
+                int64_t off = 0;
+                bool ok;
+                if constexpr (FAST) {
+                    const int64_t b = row < bnd ? base0 : base1;
+                    off = b + (int64_t)row * P.stride_tok;
+                    ok = kbase + row < n_keys && b != BAD;
                 } else {
-                    vreg[iu][j] = ok ? *(const u32x4 *)((const __bf16 *)P.v + off + dc * 8) : zero4;
+                    const int key = kbase + row;
+                    ok = key < n_keys;
+                    if (ok) {
+                        FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
+                        const uint32_t bi = fdiv((uint32_t)key, fd);
+                        const int64_t blk = bt_at((int)bi);   // widened before any product
+                        ok = blk >= 0 && blk < P.num_blocks;
+                        off = blk * P.stride_block + (int64_t)(key - (int)bi * P.block_size) * P.stride_tok +
+                              (int64_t)g * P.stride_head;
+                    }
                 }
+                dma16((const __bf16 *)P.k + (ok ? off + c * 8 : 0), kl + q * 1024);
             }
-        }
-        if constexpr (C::QK8) {
+        } else if constexpr (C::K_I8) {
+            const char *img = P.k_img + (img_base + (int64_t)kt * P.Hkv) * image_bytes(D);
 #pragma unroll
-            for (int i = 0; i < C::K8_PER_THR; ++i) {
-                const int u = tid + NTHR * i;
-                const int row = u / C::K8_CPR, c = u % C::K8_CPR;
+            for (int i = 0; i < C::K_INSTR_PER_WAVE; ++i) {
+                const int q = wave * C::K_INSTR_PER_WAVE + i;
+                dma16(img + q * 1024 + lane * 16, kl + q * 1024);
+            }
+            if (wave == NWAVE - 1) dma4(img + C::K_BYTES + lane * 4, kl + C::K_BYTES);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::K_INSTR_PER_WAVE; ++i) {
+                const int q = wave * C::K_INSTR_PER_WAVE + i;
+                const int row = q * C::KROWS_PER_INSTR + lane / C::KROW_CHUNKS;
+                const int c = pc ^ (row & C::KSWZ);
                 const int key = kbase + row;
-                const bool ok = (u < BN * C::K8_CPR) && key < n_keys;
-                const int8_t *src = (const int8_t *)P.k + ((k8_row0 + key) * P.Hkv + g) * D + c * 16;
-                kreg[i][0] = ok ? *(const u32x4 *)src : zero4;
+                dma16((const int8_t *)P.k + (key < n_keys ? ((k8_row0 + key) * P.Hkv + g) * D + c * 16 : 0),
+                      kl + q * 1024);
             }
-            if (tid < BN) {
-                const int key = kbase + tid;
-                ks_reg = key < n_keys ? P.kscale[(k8_row0 + key) * P.Hkv + g] : 0.f;
+            if (wave == NWAVE - 1) {
+                const int key = kbase + lane;
+                dma4(P.kscale + (key < n_keys ? (k8_row0 + key) * P.Hkv + g : 0), kl + C::K_BYTES);
             }
         }
     };
 
-    auto store_tile = [&](int stage) {
-        char *kt_lds = smem + stage * C::STAGE;
-        char *vt_lds = kt_lds + C::K_BYTES;
-        float *ks_lds = (float *)(kt_lds + C::KS_OFF);
-        float *vs_lds = (float *)(kt_lds + C::VS_OFF);
+    // ---- V^T tile kt (an image built by the V pass) into LDS stage `stage`
+    auto dma_v = [&](int kt, int stage) {
+        char *vl = vstage(stage);
+        const char *img = P.v_img + (img_base + (int64_t)kt * P.Hkv) * image_bytes(D);
 #pragma unroll
-        for (int iu = 0; iu < C::UPT; ++iu) {
-            const int u = tid + NTHR * iu;
-            if (u >= C::UNITS) continue;
-            const int dc = u % C::CPR, kg = u / C::CPR;
-            // K tile: row-major [64][D] bf16, 16-byte chunk c stored at c ^ (row & 7)
-            if constexpr (!C::QK8) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = kg * 4 + j;
-                    if constexpr (C::K_I8) {
-                        // 16 int8 codes -> 16 bf16 codes (exact), two chunks
-#pragma unroll
-                        for (int half = 0; half < 2; ++half) {
-                            u32x4 o;
-#pragma unroll
-                            for (int w = 0; w < 4; ++w) {
-                                const uint32_t word = kreg[iu][j][half * 2 + (w >> 1)];
-                                const int sh = (w & 1) * 16;
-                                o[w] = pack_bf16x2((float)(int8_t)((word >> sh) & 0xff),
-                                                   (float)(int8_t)((word >> (sh + 8)) & 0xff));
-                            }
-                            const int c = (dc * 2 + half) ^ (row & 7);
-                            *(u32x4 *)(kt_lds + row * (D * 2) + c * 16) = o;
-                        }
-                        if (dc == 0) ks_lds[row] = kscl[iu][j];
-                    } else {
-                        const int c = dc ^ (row & 7);
-                        *(u32x4 *)(kt_lds + row * (D * 2) + c * 16) = kreg[iu][j];
-                    }
-                }
-            }
-            // V^T tile: [D][64] fp16, 4 keys of one dim per 8-byte write
-            const int slot = vt_slot(kg * 4);
-            if constexpr (C::V_I8) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float x[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t word = vreg[iu][j][e >> 2];
-                        x[j] = (float)(int8_t)((word >> ((e & 3) * 8)) & 0xff);
-                    }
-                    const int d = dc * 16 + e;
-                    u32x2 w2 = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
-                    *(u32x2 *)(vt_lds + vt_off(d, slot)) = w2;
-                }
-                if (dc == 0) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) vs_lds[kg * 4 + j] = vscl[iu][j];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t word = vreg[iu][j][e >> 1];
-                        x[j] = (e & 1) ? bf16hi(word) : bf16lo(word);
-                    }
-                    const int d = dc * 8 + e;
-                    u32x2 w2 = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
-                    *(u32x2 *)(vt_lds + vt_off(d, slot)) = w2;
-                }
-            }
+        for (int i = 0; i < C::V_INSTR_PER_WAVE; ++i) {
+            const int q = wave * C::V_INSTR_PER_WAVE + i;
+            dma16(img + q * 1024 + lane * 16, vl + q * 1024);
         }
-        if constexpr (C::QK8) {
-#pragma unroll
-            for (int i = 0; i < C::K8_PER_THR; ++i) {
-                const int u = tid + NTHR * i;
-                if (u >= BN * C::K8_CPR) continue;
-                const int row = u / C::K8_CPR, c = u % C::K8_CPR;
-                *(u32x4 *)(kt_lds + row * D + ((c ^ (row & C::K8_SWZ)) << 4)) = kreg[i][0];
-            }
-            if (tid < BN) ks_lds[tid] = ks_reg;
+        if constexpr (C::V_I8) {
+            if (wave == 0) dma4(img + C::V_BYTES + lane * 4, vl + C::V_BYTES);
         }
     };
 
-    // ---- accumulators
-    f32x16 o[C::DB];
+    // ---- S^T = K Q^T for the 2 blocks of 32 keys of a K stage (logits in
+    // log2 units for the int8-QK arm, raw otherwise); A operands are read two
+    // k-steps ahead of the MFMAs that use them
+    auto qk_tile = [&](int stage, f32x16 (&s)[2]) {
+        const char *kl = kstage(stage);
+        auto rd = [&](int ks, int kb) -> u32x4 {
+            const int row = kb * 32 + lc;
+            const int c = (2 * ks + hf) ^ (row & C::KSWZ);
+            return *(const u32x4 *)(kl + row * C::K_ROW_BYTES + c * 16);
+        };
+        constexpr int PF = 2;
+        u32x4 a[PF + 1][2];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m_run = -INFINITY;   // running max of the log2-domain logits
-    float l_run = 0.f;         // this half-wave's share of the running sum
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < n_tiles;
-        if (more) load_tile(kt + 1);
-        const char *k_lds = smem + cur * C::STAGE;
-        const char *v_lds = k_lds + C::K_BYTES;
-
-        // ---- S^T = K Q^T for 2 blocks of 32 keys
-        f32x16 s[2];
+        for (int i = 0; i < PF && i < C::KSTEPS; ++i) {
+            a[i][0] = rd(i, 0);
+            a[i][1] = rd(i, 1);
+        }
         if constexpr (!C::QK8) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -362,13 +321,14 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < C::KSTEPS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int row = kb * 32 + lc;
-                    const int c = (2 * ks + hf) ^ (row & 7);
-                    const bf16x8 a = *(const bf16x8 *)(k_lds + row * (D * 2) + c * 16);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+                if (ks + PF < C::KSTEPS) {
+                    a[(ks + PF) % (PF + 1)][0] = rd(ks + PF, 0);
+                    a[(ks + PF) % (PF + 1)][1] = rd(ks + PF, 1);
                 }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a[ks % (PF + 1)][kb]),
+                                                                    qf[ks], s[kb], 0, 0, 0);
             }
         } else {
             i32x16 si[2];
@@ -378,13 +338,14 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 for (int i = 0; i < 16; ++i) si[kb][i] = 0;
 #pragma unroll
             for (int ks = 0; ks < C::KSTEPS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int row = kb * 32 + lc;
-                    const int c = (2 * ks + hf) ^ (row & C::K8_SWZ);
-                    const i32x4 a = *(const i32x4 *)(k_lds + row * D + c * 16);
-                    si[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, q8[ks], si[kb], 0, 0, 0);
+                if (ks + PF < C::KSTEPS) {
+                    a[(ks + PF) % (PF + 1)][0] = rd(ks + PF, 0);
+                    a[(ks + PF) % (PF + 1)][1] = rd(ks + PF, 1);
                 }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    si[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bitcast<i32x4>(a[ks % (PF + 1)][kb]),
+                                                                   q8[ks], si[kb], 0, 0, 0);
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -392,20 +353,34 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 for (int i = 0; i < 16; ++i) s[kb][i] = (float)si[kb][i];
         }
         if constexpr (C::K_SCALED) {
-            // per-key scale of the logits (keys 8*q4 + 4*hf + 0..3 of each block)
-            const float *ks_lds = (const float *)(k_lds + C::KS_OFF);
+            // per-key scale; the int8-QK arm also folds in sq * scale * log2e, so an
+            // all-zero query row (sq = 0) gives zero logits, never 0 * inf
+            const float *ks_lds = (const float *)(kl + C::K_BYTES);
+            const float f = C::QK8 ? lfac : 1.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const f32x4 kk = *(const f32x4 *)(ks_lds + kb * 32 + q4 * 8 + hf * 4);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) s[kb][q4 * 4 + i] *= kk[i];
+                    for (int i = 0; i < 4; ++i) s[kb][q4 * 4 + i] *= kk[i] * f;
                 }
         }
+    };
 
-        // ---- causal / tail mask (only tiles that reach past the first column's position)
-        if (kt * BN + BN - 1 > pos_min) {
+    // ---- accumulators
+    f32x16 o[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    const float smfac = C::QK8 ? 1.0f : lfac;   // logit -> log2 units in the softmax
+    float m_run = -INFINITY;   // running (lazy) max of the log2-domain logits
+    float l_run = 0.f;         // this half-wave's share of the running sum
+
+    // softmax of one tile's logits, in place: s becomes P (relative to m_run)
+    auto softmax_tile = [&](f32x16 (&s)[2], int kt) {
+        if (kt * BN + BN - 1 > pos_min) {   // tiles that reach past the first column
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -414,61 +389,89 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                     if (key > my_pos) s[kb][i] = -INFINITY;
                 }
         }
-
-        // ---- online softmax (log2 domain)
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = max_halves(mx);
-        const float m_new = fmaxf(m_run, mx * lfac);
-        const float alpha = exp2_fast(m_run - m_new);
+        mx = max_halves(mx) * smfac;
+        if (__any(mx > m_run + RESCALE_SLACK)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = exp2_fast(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+            m_run = m_new;
+        }
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float pv = exp2_fast(fmaf(s[kb][i], lfac, -m_new));
+                const float pv = exp2_fast(fmaf(s[kb][i], smfac, -m_run));
                 s[kb][i] = pv;
                 psum += pv;
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        l_run += psum;
+    };
 
-        // ---- O^T += V^T P^T, 4 steps of 16 keys
+    // ---- O^T += V^T P^T for one V stage: 4 steps of 16 keys x DB blocks of 32
+    // dims; A operands are read PF ahead of the MFMAs that use them
+    auto pv_tile = [&](int stage, const f32x16 (&s)[2]) {
+        const char *vl = vstage(stage);
+        auto rd = [&](int i) -> f16x8 {
+            const int st = i / C::DB, db = i % C::DB;
+            const int d = db * 32 + lc;
+            const int c = (2 * st + hf) ^ vt_swz(d);
+            return *(const f16x8 *)(vl + d * (BN * 2) + c * 16);
+        };
+        constexpr int NOPS = 4 * C::DB;
+        constexpr int PF = 3;
+        f16x8 a[PF + 1];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int kb = st >> 1, base = (st & 1) * 8;
-            f16x8 pb;
-            if constexpr (C::V_I8) {
-                // fold each key's V scale into P: keys 16*st + 8*(i/4) + 4*hf + i%4
-                const float *vs_lds = (const float *)(k_lds + C::VS_OFF);
-                const f32x4 v0 = *(const f32x4 *)(vs_lds + 16 * st + 4 * hf);
-                const f32x4 v1 = *(const f32x4 *)(vs_lds + 16 * st + 8 + 4 * hf);
+        for (int i = 0; i < PF; ++i) a[i] = rd(i);
+        f16x8 pb;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pb[i] = (_Float16)(s[kb][base + i] * v0[i]);
-                    pb[4 + i] = (_Float16)(s[kb][base + 4 + i] * v1[i]);
+        for (int i = 0; i < NOPS; ++i) {
+            const int st = i / C::DB, db = i % C::DB;
+            if (i + PF < NOPS) a[(i + PF) % (PF + 1)] = rd(i + PF);
+            if (db == 0) {
+                const int kb = st >> 1, base = (st & 1) * 8;
+                if constexpr (C::V_I8) {
+                    // fold each key's V scale into P: keys 16*st + 8*(j/4) + 4*hf + j%4
+                    const float *vs_lds = (const float *)(vl + C::V_BYTES);
+                    const f32x4 v0 = *(const f32x4 *)(vs_lds + 16 * st + 4 * hf);
+                    const f32x4 v1 = *(const f32x4 *)(vs_lds + 16 * st + 8 + 4 * hf);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pb[j] = (_Float16)(s[kb][base + j] * v0[j]);
+                        pb[4 + j] = (_Float16)(s[kb][base + 4 + j] * v1[j]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pb[j] = (_Float16)s[kb][base + j];
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pb[i] = (_Float16)s[kb][base + i];
             }
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const int d = db * 32 + lc;
-                const int c = (2 * st + hf) ^ vt_swz(d);
-                const f16x8 a = *(const f16x8 *)(v_lds + d * (BN * 2) + c * 16);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, o[db], 0, 0, 0);
-            }
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i % (PF + 1)], pb, o[db], 0, 0, 0);
         }
+    };
 
-        if (more) store_tile(cur ^ 1);
+    // ---- main loop: tile kt is in LDS stage kt & 1 while tile kt+1 streams in
+    f32x16 s[2];
+    dma_k(0, 0);
+    dma_v(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < n_tiles; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < n_tiles) {
+            dma_k(kt + 1, cur ^ 1);
+            dma_v(kt + 1, cur ^ 1);
+        }
+        qk_tile(cur, s);
+        softmax_tile(s, kt);
+        pv_tile(cur, s);
         __syncthreads();
     }
 
@@ -495,10 +498,18 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 
 template <int D, int KIND>
 static hipError_t launch_t(bool out_bf16, const AttnParams &p, dim3 grid, hipStream_t s) {
-    if (out_bf16)
-        hipLaunchKernelGGL((attn_kernel<D, KIND, true>), grid, dim3(NTHR), 0, s, p);
-    else
-        hipLaunchKernelGGL((attn_kernel<D, KIND, false>), grid, dim3(NTHR), 0, s, p);
+    const bool fast = p.block_size >= BN;
+    if (out_bf16) {
+        if (fast)
+            hipLaunchKernelGGL((attn_kernel<D, KIND, true, true>), grid, dim3(NTHR), 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_kernel<D, KIND, true, false>), grid, dim3(NTHR), 0, s, p);
+    } else {
+        if (fast)
+            hipLaunchKernelGGL((attn_kernel<D, KIND, false, true>), grid, dim3(NTHR), 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_kernel<D, KIND, false, false>), grid, dim3(NTHR), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -1,0 +1,172 @@
+// pa_images.hip -- one pass per call that lays a request's V (and, for the
+// int8-KV exact arm, its K) out as per-tile images in the attention kernel's
+// LDS layout (pa_layout.h).
+//
+// Why a pass: the PV product wants V transposed, in fp16 (P keeps 11
+// significant bits there), with the keys of each 16-key group in the order
+// the S accumulator hands them over.  Every workgroup of a (request, KV head)
+// streams the same V, so doing that gather / convert / transpose inside the
+// attention kernel repeats it once per workgroup (64 times for a 2,048-token
+// chunk with 4 q heads per KV head) and costs the attention loop registers.
+// Done once here, the attention kernel moves each tile with plain 1 KB
+// direct-to-LDS copies.  This is the same trade vllm.cpp PR #3360 makes for
+// fp8 KV ("What changed": dequantise once, not on every re-stream).
+//
+// The pass reads the paged pool through the block table with 64-bit offsets,
+// stages each tile through LDS (V^T is a transpose) and writes the image with
+// coalesced 16-byte stores.  int8 codes are kept as codes (exact in bf16 and
+// fp16) and their per-token-head scales go to the image's scale vector.
+// Keys at or past the context length are zero (scale 0).
+#include "pa_device.h"
+#include "pa_kernels.h"
+#include "pa_layout.h"
+
+namespace pa {
+
+constexpr int IT = 256;   // threads per workgroup
+
+__device__ __forceinline__ bool img_row(const ImageParams &P, int r, int key, int g, int64_t &off,
+                                        int64_t &soff) {
+    FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
+    const uint32_t bi = fdiv((uint32_t)key, fd);
+    const uint32_t slot = (uint32_t)key - bi * (uint32_t)P.block_size;
+    const int64_t blk = (int64_t)P.bt[(int64_t)r * P.stride_bt + bi];   // widen before any product
+    if (blk < 0 || blk >= P.num_blocks) return false;
+    off = blk * P.stride_block + (int64_t)slot * P.stride_tok + (int64_t)g * P.stride_head;
+    soff = blk * P.stride_sblock + (int64_t)slot * P.stride_stok + g;
+    return true;
+}
+
+__device__ __forceinline__ bool img_tile(const ImageParams &P, int &t, int &g, int &r, int &L) {
+    t = blockIdx.x;
+    g = blockIdx.y;
+    r = blockIdx.z;
+    L = P.ctx_lens[r];
+    if (L <= 0 || L > P.max_ctx || (int64_t)(L - 1) / P.block_size >= P.stride_bt) return false;
+    return t * TILE_KEYS < L;
+}
+
+// V^T image: [D][64] fp16 + 64 scales.  One unit = 4 consecutive keys x one
+// 16-byte chunk of the source row; its 4 x 8 (bf16) or 4 x 16 (int8) values are
+// written to LDS as 8-byte groups of 4 keys of one dim.
+template <int D, bool SRC_I8>
+__global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
+    constexpr int CPR = (SRC_I8 ? D : 2 * D) / 16;
+    constexpr int UNITS = 16 * CPR;
+    constexpr int V_BYTES = TILE_KEYS * D * 2;
+    __shared__ __attribute__((aligned(16))) char img[V_BYTES + TILE_KEYS * 4];
+    int t, g, r, L;
+    if (!img_tile(P, t, g, r, L)) return;
+    const int tid = threadIdx.x;
+    float *scl = (float *)(img + V_BYTES);
+    for (int u = tid; u < UNITS; u += IT) {
+        const int dc = u % CPR, kg = u / CPR;
+        u32x4 w[4];
+        float s[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key = t * TILE_KEYS + kg * 4 + j;
+            int64_t off = 0, soff = 0;
+            const bool ok = key < L && img_row(P, r, key, g, off, soff);
+            if (SRC_I8) {
+                w[j] = ok ? *(const u32x4 *)((const int8_t *)P.src + off + dc * 16) : u32x4{0, 0, 0, 0};
+                s[j] = ok ? P.src_scales[soff] : 0.f;
+            } else {
+                w[j] = ok ? *(const u32x4 *)((const __bf16 *)P.src + off + dc * 8) : u32x4{0, 0, 0, 0};
+                s[j] = 0.f;
+            }
+        }
+        const int slot = vt_slot(kg * 4);
+        if (SRC_I8) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = (float)(int8_t)((w[j][e >> 2] >> ((e & 3) * 8)) & 0xff);
+                *(u32x2 *)(img + vt_off(dc * 16 + e, slot)) =
+                    u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = (e & 1) ? bf16hi(w[j][e >> 1]) : bf16lo(w[j][e >> 1]);
+                *(u32x2 *)(img + vt_off(dc * 8 + e, slot)) =
+                    u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
+            }
+        }
+        if (dc == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) scl[kg * 4 + j] = s[j];
+        }
+    }
+    __syncthreads();
+    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * image_bytes(D);
+    constexpr int CHUNKS = (V_BYTES + TILE_KEYS * 4) / 16;
+    for (int c = tid; c < CHUNKS; c += IT) *(u32x4 *)(dst + c * 16) = *(const u32x4 *)(img + c * 16);
+}
+
+// K image of an int8 pool: [64][D] bf16 codes (exact), XOR-swizzled chunks, + 64 scales.
+template <int D>
+__global__ __launch_bounds__(IT) void k_image_kernel(const ImageParams P) {
+    constexpr int CPR = D / 16;                      // source chunks (16 codes) per row
+    constexpr int KSWZ = ktile_swz_mask(2 * D);
+    int t, g, r, L;
+    if (!img_tile(P, t, g, r, L)) return;
+    const int tid = threadIdx.x;
+    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * image_bytes(D);
+    float *scl = (float *)(dst + TILE_KEYS * D * 2);
+    for (int u = tid; u < TILE_KEYS * CPR; u += IT) {
+        const int row = u / CPR, dc = u % CPR;
+        const int key = t * TILE_KEYS + row;
+        int64_t off = 0, soff = 0;
+        const bool ok = key < L && img_row(P, r, key, g, off, soff);
+        const u32x4 w = ok ? *(const u32x4 *)((const int8_t *)P.src + off + dc * 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t word = w[half * 2 + (q >> 1)];
+                const int sh = (q & 1) * 16;
+                o[q] = pack_bf16x2((float)(int8_t)((word >> sh) & 0xff),
+                                   (float)(int8_t)((word >> (sh + 8)) & 0xff));
+            }
+            const int c = (dc * 2 + half) ^ (row & KSWZ);
+            *(u32x4 *)(dst + row * (D * 2) + c * 16) = o;
+        }
+        if (dc == 0) scl[row] = ok ? P.src_scales[soff] : 0.f;
+    }
+}
+
+template <int D>
+static hipError_t launch_images_d(const ImageParams &p, bool v_int8, bool k_image, hipStream_t s) {
+    dim3 grid((uint32_t)p.tiles, (uint32_t)p.Hkv, (uint32_t)p.num_reqs);
+    ImageParams pv = p;
+    if (v_int8) {
+        hipLaunchKernelGGL((v_image_kernel<D, true>), grid, dim3(IT), 0, s, pv);
+    } else {
+        hipLaunchKernelGGL((v_image_kernel<D, false>), grid, dim3(IT), 0, s, pv);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !k_image) return e;
+    ImageParams pk = p;
+    pk.src = p.src2;
+    pk.src_scales = p.src2_scales;
+    pk.dst = p.dst2;
+    hipLaunchKernelGGL((k_image_kernel<D>), grid, dim3(IT), 0, s, pk);
+    return hipGetLastError();
+}
+
+hipError_t launch_images(const ImageParams &p, bool v_int8, bool k_image, hipStream_t s) {
+    if (p.tiles <= 0) return hipSuccess;
+    switch (p.D) {
+        case 64: return launch_images_d<64>(p, v_int8, k_image, s);
+        case 128: return launch_images_d<128>(p, v_int8, k_image, s);
+        case 256: return launch_images_d<256>(p, v_int8, k_image, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pa

@@ -29,8 +29,10 @@ struct AttnParams {
     const void *q;
     const void *k;              // bf16 / int8 pool, or dense k8
     const void *v;              // bf16 / int8 pool
-    const float *kscale;        // int8 pool scales, or ks (int8-QK)
-    const float *vscale;
+    const float *kscale;        // ks (int8-QK)
+    const char *v_img;          // V^T tile images (workspace), [R][T][Hkv] images
+    const char *k_img;          // K tile images of an int8 pool (int8-KV exact arm)
+    int64_t img_tiles;          // T: tiles per request in the image arrays
     void *out;
 };
 
@@ -60,9 +62,29 @@ struct PassParams {
     int32_t src_int8;           // K passes: 1 int8 pool, 0 bf16 pool
 };
 
+// Tile-image passes (pa_images.hip).
+struct ImageParams {
+    const int32_t *bt;
+    int64_t stride_bt;
+    const int32_t *ctx_lens;
+    int32_t num_reqs, Hkv, D, block_size, max_ctx;
+    FastDivHost bsdiv;
+    int64_t num_blocks;
+    int64_t stride_block, stride_tok, stride_head;
+    int64_t stride_sblock, stride_stok;
+    int64_t tiles;              // T: tiles per request
+    const void *src;            // V pool
+    const float *src_scales;    // V scales (int8 pool)
+    const void *src2;           // K pool (int8 exact arm)
+    const float *src2_scales;
+    void *dst;                  // V images
+    void *dst2;                 // K images
+};
+
 // launchers: return hipError_t of the launch
 hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,
                             int32_t max_q_len, hipStream_t stream);
+hipError_t launch_images(const ImageParams &p, bool v_int8, bool k_image, hipStream_t stream);
 hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);
 hipError_t launch_k_quant(const PassParams &p, hipStream_t stream);
 hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t stream);

@@ -18,11 +18,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpaged_kv_prefill.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
+PA_ERR_WORKSPACE = -6
+PA_ENTRY_PREFILL_BF16, PA_ENTRY_PREFILL_INT8KV, PA_ENTRY_PREFILL_INT8QK = 1, 2, 3
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_INT8, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_k_stats", "pa_k_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_gather_kv",
-                "pa_status_string", "pa_build_id"]
+                "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
 
 
 class PagedArgs(C.Structure):
@@ -54,13 +56,13 @@ def lib():
                 f"{LIB_PATH} is not built; run `python -m paged_kv_prefill_amd.build` "
                 "(there is no CPU fallback)")
         L = C.CDLL(LIB_PATH)
-        vp, i32, pa = C.c_void_p, C.c_int32, C.POINTER(PagedArgs)
+        vp, i32, sz, pa = C.c_void_p, C.c_int32, C.c_size_t, C.POINTER(PagedArgs)
         sig = {
-            "pa_prefill_bf16": [pa, vp, vp, vp, vp, i32, vp],
-            "pa_prefill_int8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp],
+            "pa_prefill_bf16": [pa, vp, vp, vp, vp, i32, vp, sz, vp],
+            "pa_prefill_int8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
             "pa_k_stats": [pa, vp, i32, vp, vp, vp, vp],
             "pa_k_quant": [pa, vp, i32, vp, vp, vp, vp, vp],
-            "pa_prefill_int8qk": [pa, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp],
+            "pa_prefill_int8qk": [pa, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
             "pa_fp8_dense_dequant": [pa, vp, vp, vp, vp, i32, vp, vp, vp],
             "pa_gather_kv": [pa, vp, i32, vp, vp, vp],
         }
@@ -68,6 +70,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = argt
             fn.restype = i32
+        L.pa_workspace_bytes.argtypes = [pa, i32]
+        L.pa_workspace_bytes.restype = sz
         L.pa_status_string.argtypes = [i32]
         L.pa_status_string.restype = C.c_char_p
         L.pa_build_id.argtypes = []
@@ -149,19 +153,39 @@ class Paged:
 
 
 # ------------------------------------------------------------------ entry points
-def pa_prefill_bf16(p: Paged, q, k_pool, v_pool, out, stream=None):
+def pa_workspace_bytes(p: Paged, entry: int) -> int:
+    return int(lib().pa_workspace_bytes(C.byref(p.args()), int(entry)))
+
+
+def workspace(p: Paged, entry: int, device=None) -> torch.Tensor:
+    """A device buffer of pa_workspace_bytes(p, entry) bytes (torch-owned)."""
+    n = pa_workspace_bytes(p, entry)
+    if n <= 0:
+        raise PagedKVError("invalid arguments for pa_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device or p.block_table.device)
+
+
+def _ws(p, entry, ws):
+    ws = workspace(p, entry) if ws is None else ws
+    return ws, C.c_void_p(ws.data_ptr()), C.c_size_t(ws.numel() * ws.element_size())
+
+
+def pa_prefill_bf16(p: Paged, q, k_pool, v_pool, out, ws=None, stream=None):
     a = p.args()
     dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
-    _check(lib().pa_prefill_bf16(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(out), dt,
+    ws, wp, wn = _ws(p, PA_ENTRY_PREFILL_BF16, ws)
+    _check(lib().pa_prefill_bf16(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(out), dt, wp, wn,
                                  _stream(stream)), "pa_prefill_bf16")
     return out
 
 
-def pa_prefill_int8kv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, out, stream=None):
+def pa_prefill_int8kv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, out, ws=None,
+                      stream=None):
     a = p.args()
     dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    ws, wp, wn = _ws(p, PA_ENTRY_PREFILL_INT8KV, ws)
     _check(lib().pa_prefill_int8kv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(k_scales),
-                                   _p(v_scales), _p(out), dt, _stream(stream)),
+                                   _p(v_scales), _p(out), dt, wp, wn, _stream(stream)),
            "pa_prefill_int8kv")
     return out
 
@@ -184,12 +208,14 @@ def pa_k_quant(p: Paged, k_pool, k_pool_scales, cu_ctx, ks, k8, stream=None):
     return k8
 
 
-def pa_prefill_int8qk(p: Paged, q, k8, ks, cu_ctx, v_pool, v_scales, out, stream=None):
+def pa_prefill_int8qk(p: Paged, q, k8, ks, cu_ctx, v_pool, v_scales, out, ws=None,
+                      stream=None):
     a = p.args()
     dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    ws, wp, wn = _ws(p, PA_ENTRY_PREFILL_INT8QK, ws)
     _check(lib().pa_prefill_int8qk(C.byref(a), _p(q), _p(k8), _p(ks), _p(cu_ctx), _p(v_pool),
-                                   _kdtype(v_pool), _p(v_scales), _p(out), dt, _stream(stream)),
-           "pa_prefill_int8qk")
+                                   _kdtype(v_pool), _p(v_scales), _p(out), dt, wp, wn,
+                                   _stream(stream)), "pa_prefill_int8qk")
     return out
 
 

@@ -67,7 +67,7 @@ def test_argument_errors_return_status(kw, code):
     L = ops.lib()
     a = _args(**kw)
     p = C.c_void_p(4096)
-    rc = L.pa_prefill_bf16(C.byref(a), p, p, p, p, ops.PA_DTYPE_F32, None)
+    rc = L.pa_prefill_bf16(C.byref(a), p, p, p, p, ops.PA_DTYPE_F32, p, 1 << 40, None)
     assert rc == code
 
 
@@ -76,19 +76,34 @@ def test_entry_point_specific_errors():
     a = _args()
     p = C.c_void_p(4096)
     odd = C.c_void_p(4100)
-    assert L.pa_prefill_bf16(None, p, p, p, p, 0, None) == ops.PA_ERR_NULL
-    assert L.pa_prefill_bf16(C.byref(a), None, p, p, p, 0, None) == ops.PA_ERR_NULL
-    assert L.pa_prefill_bf16(C.byref(a), p, p, p, p, 7, None) == ops.PA_ERR_UNSUPPORTED
-    assert L.pa_prefill_bf16(C.byref(a), odd, p, p, p, 0, None) == ops.PA_ERR_SHAPE
-    assert L.pa_prefill_int8kv(C.byref(a), p, p, p, None, p, p, 0, None) == ops.PA_ERR_NULL
+    big = 1 << 40
+    assert L.pa_prefill_bf16(None, p, p, p, p, 0, p, big, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16(C.byref(a), None, p, p, p, 0, p, big, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16(C.byref(a), p, p, p, p, 7, p, big, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_prefill_bf16(C.byref(a), odd, p, p, p, 0, p, big, None) == ops.PA_ERR_SHAPE
+    assert L.pa_prefill_bf16(C.byref(a), p, p, p, p, 0, None, big, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16(C.byref(a), p, p, p, p, 0, p, 16, None) == ops.PA_ERR_WORKSPACE
+    assert L.pa_prefill_int8kv(C.byref(a), p, p, p, None, p, p, 0, p, big, None) == ops.PA_ERR_NULL
     assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_F32, None, p, p, None) == ops.PA_ERR_UNSUPPORTED
     assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_INT8, None, p, p, None) == ops.PA_ERR_NULL
     assert L.pa_k_quant(C.byref(a), p, ops.PA_DTYPE_BF16, None, p, p, None, None) == ops.PA_ERR_NULL
     assert L.pa_prefill_int8qk(C.byref(a), p, p, p, p, p, ops.PA_DTYPE_FP8_E4M3, None, p, 0,
-                               None) == ops.PA_ERR_UNSUPPORTED
+                               p, big, None) == ops.PA_ERR_UNSUPPORTED
     assert L.pa_fp8_dense_dequant(C.byref(a), p, p, p, p, 8, p, p, None) == ops.PA_ERR_SHAPE
     assert L.pa_fp8_dense_dequant(C.byref(a), p, p, None, p, 16, p, p, None) == ops.PA_ERR_NULL
     assert L.pa_gather_kv(C.byref(a), p, 4, p, p, None) == ops.PA_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula():
+    """num_reqs * ceil(max_ctx / 64) * Hkv images of 128 * D + 256 bytes."""
+    L = ops.lib()
+    a = _args(num_reqs=3, max_ctx_len=130, num_kv_heads=2, head_dim=64)
+    img = 128 * 64 + 256
+    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_BF16) == 3 * 3 * 2 * img
+    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8QK) == 3 * 3 * 2 * img
+    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8KV) == 2 * 3 * 3 * 2 * img
+    assert L.pa_workspace_bytes(C.byref(a), 99) == 0
+    assert L.pa_workspace_bytes(C.byref(_args(num_q_heads=3)), ops.PA_ENTRY_PREFILL_BF16) == 0
 
 
 def test_pool_geometry_matches_pages():
