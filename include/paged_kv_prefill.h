@@ -43,8 +43,9 @@
  *     length must respect them (rows beyond are not computed).  Requests whose
  *     device lengths are inconsistent (Lq > L, L beyond what the block-table row
  *     can hold, L > max_ctx_len) are skipped and their outputs left untouched.
- *   - Block ids outside [0, num_blocks) are a caller error; the kernels read
- *     such rows as zeros instead of touching memory outside the pool.
+ *   - Block ids outside [0, num_blocks) are a caller error: the kernels never
+ *     touch memory outside the pool for them (they read zeros or a row of
+ *     block 0 instead) and the outputs that depend on them are unspecified.
  */
 #ifndef PAGED_KV_PREFILL_H
 #define PAGED_KV_PREFILL_H
@@ -167,8 +168,10 @@ int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8
 
 /*
  * pa_workspace_bytes -- device workspace an attention entry point needs for
- * these arguments: num_reqs * ceil(max_ctx_len / 64) * num_kv_heads tile images
- * of 128 * head_dim + 256 bytes (twice that for PA_ENTRY_PREFILL_INT8KV).
+ * these arguments: n = num_reqs * ceil(max_ctx_len / 64) * num_kv_heads V tile
+ * images of 144 * head_dim + 256 bytes (fp16 rows of 64 keys padded to 72,
+ * plus scales), and for PA_ENTRY_PREFILL_INT8KV n more K tile images of
+ * 128 * head_dim + 256 bytes.
  * Returns 0 for invalid arguments or an unknown entry.
  */
 size_t pa_workspace_bytes(const pa_paged_args *args, int32_t entry);

@@ -115,8 +115,9 @@ int64_t image_count(const pa_paged_args *a) {
 // bytes of workspace an attention entry point needs: V^T tile images, plus K
 // tile images for the int8-KV exact arm
 int64_t workspace_need(const pa_paged_args *a, int32_t entry) {
-    const int64_t n = image_count(a) * image_bytes(a->head_dim);
-    return entry == PA_ENTRY_PREFILL_INT8KV ? 2 * n : n;
+    const int64_t n = image_count(a);
+    return n * v_image_bytes(a->head_dim) +
+           (entry == PA_ENTRY_PREFILL_INT8KV ? n * k_image_bytes(a->head_dim) : 0);
 }
 
 int check_workspace(const pa_paged_args *a, int32_t entry, void *ws, size_t bytes) {
@@ -126,7 +127,7 @@ int check_workspace(const pa_paged_args *a, int32_t entry, void *ws, size_t byte
     return PA_OK;
 }
 
-ImageParams image_params(const pa_paged_args *a, void *ws) {
+ImageParams image_params(const pa_paged_args *a, void *ws, int kind) {
     ImageParams p{};
     p.bt = a->block_table;
     p.stride_bt = a->stride_bt;
@@ -145,7 +146,8 @@ ImageParams image_params(const pa_paged_args *a, void *ws) {
     p.stride_stok = a->stride_stok;
     p.tiles = tiles_per_request(a->max_ctx_len);
     p.dst = ws;
-    p.dst2 = (char *)ws + image_count(a) * image_bytes(a->head_dim);
+    p.v_rpi = attn_rows_per_copy(kind, a->head_dim);
+    p.dst2 = (char *)ws + image_count(a) * v_image_bytes(a->head_dim);
     return p;
 }
 
@@ -162,7 +164,7 @@ int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, c
     if (!k_pool || !v_pool) return PA_ERR_NULL;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
     if ((rc = check_workspace(a, PA_ENTRY_PREFILL_BF16, workspace, workspace_bytes))) return rc;
-    ImageParams ip = image_params(a, workspace);
+    ImageParams ip = image_params(a, workspace, KIND_BF16);
     ip.src = v_pool;
     if ((rc = launched(launch_images(ip, false, false, stream)))) return rc;
     AttnParams p = attn_params(a);
@@ -186,7 +188,7 @@ int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_poo
     if ((rc = check_scales(a, k_scales)) || (rc = check_scales(a, v_scales))) return rc;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
     if ((rc = check_workspace(a, PA_ENTRY_PREFILL_INT8KV, workspace, workspace_bytes))) return rc;
-    ImageParams ip = image_params(a, workspace);
+    ImageParams ip = image_params(a, workspace, KIND_I8KV);
     ip.src = v_pool;
     ip.src_scales = v_scales;
     ip.src2 = k_pool;
@@ -250,7 +252,8 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     if (v_dtype == PA_DTYPE_INT8 && (rc = check_scales(a, v_scales))) return rc;
     if (!aligned16(k8) || !aligned16(v_pool)) return PA_ERR_SHAPE;
     if ((rc = check_workspace(a, PA_ENTRY_PREFILL_INT8QK, workspace, workspace_bytes))) return rc;
-    ImageParams ip = image_params(a, workspace);
+    const int kind = v_dtype == PA_DTYPE_INT8 ? KIND_QK8_VI8 : KIND_QK8_VBF16;
+    ImageParams ip = image_params(a, workspace, kind);
     ip.src = v_pool;
     ip.src_scales = v_scales;
     if ((rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8, false, stream)))) return rc;
@@ -262,7 +265,6 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     p.v_img = (const char *)workspace;
     p.img_tiles = ip.tiles;
     p.out = out;
-    const int kind = v_dtype == PA_DTYPE_INT8 ? KIND_QK8_VI8 : KIND_QK8_VBF16;
     return launched(launch_attention(kind, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
                                      a->max_q_len, stream));
 }

@@ -29,14 +29,18 @@
 //
 // Data movement.  Tiles are double-buffered in LDS and move with gfx950's
 // direct global-to-LDS copies (global_load_lds_dwordx4, 1 KB per wave
-// instruction, no registers): K straight from the paged pool (each lane
-// fetches the chunk that the layout's XOR swizzle puts under it; the block
-// table row is cached in LDS, and with block_size >= 64 a tile spans at most
-// two blocks, so the block bases are wave-uniform scalars), V from the per-tile
-// V^T images that pa_images.hip builds once per call.  The copies of tile t+1
-// are issued before the MFMAs of tile t; one barrier per tile.  The running
-// maximum is updated lazily: O and the row sum are rescaled only when some
-// column's maximum grows by more than 2^8 (log2 units).
+// instruction, no registers).  A K copy takes the rows of 1024 / R consecutive
+// keys (R = bytes per key row); with block_size a multiple of 16 those keys
+// sit in one cache block, so the copy's address is a wave-uniform scalar (block
+// id from the block-table row cached in LDS, widened to 64 bits) plus a
+// per-lane constant, and the loop spends no vector instructions on it.  V comes
+// from the per-tile V^T images that pa_images.hip builds once per call.  The
+// tile layouts (pa_layout.h) pad rows instead of swizzling them, so every
+// operand read of a lane is one base register plus an immediate offset and no
+// LDS read conflicts.  The copies of tile t+1 are issued before the MFMAs of
+// tile t; one barrier per tile.  The running maximum is updated lazily: O and
+// the row sum are rescaled only when some column's maximum grows by more than
+// 2^8 (log2 units).
 //
 // The int8-QK arm replaces the QK MFMA with v_mfma_i32_32x32x32_i8 on the
 // int8 K written by the K-quant pass and on Q quantised per (token, head) in
@@ -69,23 +73,38 @@ struct AttnCfg {
     static constexpr bool K_PAGED = (KIND == KIND_BF16);   // K straight from the bf16 pool
     static constexpr bool K_SCALED = K_I8 || QK8;          // logits need a per-key scale
     static constexpr int K_ROW_BYTES = QK8 ? D : 2 * D;
-    static constexpr int K_BYTES = BN * K_ROW_BYTES;
-    static constexpr int V_BYTES = BN * D * 2;
+    static constexpr int RPI = 1024 / K_ROW_BYTES;         // key rows per 1 KB K copy
+    static constexpr int KCOPIES = BN / RPI;               // K copies per tile
+    static constexpr int KCPR = K_ROW_BYTES / 16;          // lanes per key row in a copy
+    static constexpr int K_BYTES = KCOPIES * K_COPY_STRIDE;
+    static constexpr int V_BYTES = vt_tile_bytes(D);
+    static constexpr int VCOPIES = V_BYTES / 1024;
     static constexpr int KSTAGE = K_BYTES + (K_SCALED ? BN * 4 : 0);
     static constexpr int VSTAGE = V_BYTES + (V_I8 ? BN * 4 : 0);
     static constexpr int BT_OFF = 2 * KSTAGE + 2 * VSTAGE;
     static constexpr int BT_CAP = K_PAGED ? ((LDS_MAX - BT_OFF) / 4 < 4096 ? (LDS_MAX - BT_OFF) / 4 : 4096) : 0;
     static constexpr int LDS = BT_OFF + BT_CAP * 4;
-    static constexpr int KROW_CHUNKS = K_ROW_BYTES / 16;
-    static constexpr int KROWS_PER_INSTR = 64 / KROW_CHUNKS;
-    static constexpr int K_INSTR_PER_WAVE = K_BYTES / 1024 / NWAVE;
-    static constexpr int V_INSTR_PER_WAVE = V_BYTES / 1024 / NWAVE;
-    static constexpr int KSWZ = ktile_swz_mask(K_ROW_BYTES);
+    static constexpr int K_PER_WAVE = KCOPIES / NWAVE;
+    static constexpr int V_PER_WAVE = (VCOPIES + NWAVE - 1) / NWAVE;
     static constexpr int KSTEPS = QK8 ? D / 32 : D / 16;
     static constexpr int DB = D / 32;
-    static_assert(K_INSTR_PER_WAVE >= 1 && V_INSTR_PER_WAVE >= 1, "tile too small");
+    static constexpr int KB_STEP = (32 / KCOPIES) * K_ROW_BYTES;   // LDS bytes between key blocks
+    // key offset of the upper half-wave's accumulator rows (positions +4)
+    static constexpr int HSTEP = tile_key(4, RPI) - tile_key(0, RPI);
+    static_assert(K_PER_WAVE >= 1 && KCOPIES % NWAVE == 0, "K copies per wave");
+    static_assert(V_BYTES % 1024 == 0, "V^T tile is whole copies");
+    static_assert(KB_STEP == 512, "key block stride");
     static_assert(LDS <= LDS_MAX, "LDS budget");
 };
+
+// the half-wave bit of an accumulator row moves its key by a fixed step
+__host__ __device__ constexpr bool hstep_uniform(int rpi) {
+    for (int p = 0; p < 64; ++p)
+        if (!(p & 4) && tile_key(p + 4, rpi) - tile_key(p, rpi) != tile_key(4, rpi) - tile_key(0, rpi))
+            return false;
+    return true;
+}
+static_assert(hstep_uniform(2) && hstep_uniform(4) && hstep_uniform(8) && hstep_uniform(16), "HSTEP");
 
 __device__ __forceinline__ void dma16(const void *src, char *lds) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
@@ -197,88 +216,106 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     auto bt_at = [&](int i) -> int64_t {
         return (int64_t)(i < C::BT_CAP ? bt_lds[i] : P.bt[bt_row + i]);
     };
+    // wave-uniform block-table entry through the scalar cache (read only)
+    auto bt_scalar = [&](int i) -> int {
+        return ((const __attribute__((address_space(4))) int32_t *)P.bt)[bt_row + i];
+    };
 
     const int64_t img_base = ((int64_t)r * P.img_tiles) * P.Hkv + g;   // image index of tile 0
     const int64_t k8_row0 = C::QK8 ? (int64_t)P.cu_ctx[r] : 0;
     auto kstage = [&](int s) { return smem + s * C::KSTAGE; };
     auto vstage = [&](int s) { return smem + 2 * C::KSTAGE + s * C::VSTAGE; };
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-    // ---- K tile kt into LDS stage `stage`.  Wave instruction q fills bytes
-    // [q KB, q KB + 1 KB): lane l lands at chunk l % KROW_CHUNKS of row
-    // q * KROWS_PER_INSTR + l / KROW_CHUNKS, so it fetches the logical chunk the
-    // XOR swizzle maps there.  Rows past the context fetch a mapped dummy
-    // address; their logits are masked.
+    // ---- per-lane constants of the K copies: lane l moves chunk l % KCPR of
+    // key row l / KCPR of its copy (the copy's rpi keys are consecutive)
+    const int k_sub = lane / C::KCPR, k_chunk = lane % C::KCPR;
+    const int64_t stb = P.stride_tok * 2, sbb = P.stride_block * 2, ghb = (int64_t)g * P.stride_head * 2;
+    const int64_t k8_rowb = (int64_t)P.Hkv * D;                        // bytes per dense k8 row
+    const uint32_t nb32 = (uint32_t)(P.num_blocks < INT32_MAX ? P.num_blocks : INT32_MAX);
+    uint32_t k_lane_src;
+    if constexpr (C::K_PAGED) k_lane_src = (uint32_t)(k_sub * stb + k_chunk * 16);
+    else if constexpr (C::QK8) k_lane_src = (uint32_t)(k_sub * k8_rowb + k_chunk * 16);
+    else k_lane_src = (uint32_t)(lane * 16);
+    const int k_key_lane = tile_key(lane, C::RPI);                     // key of scale slot `lane`
+
+    // ---- K tile kt into LDS stage `stage`: copy q (keys q*rpi ...) lands at
+    // q * K_COPY_STRIDE.  Keys past the context read a mapped dummy row; their
+    // logits are masked.
     auto dma_k = [&](int kt, int stage) {
         char *kl = kstage(stage);
         const int kbase = kt * BN;
-        const int pc = lane % C::KROW_CHUNKS;
         if constexpr (C::K_PAGED) {
-            int64_t base0 = 0, base1 = 0;
-            int bnd = BN;
-            constexpr int64_t BAD = INT64_MIN;
+            const char *kpool = (const char *)P.k;
             if constexpr (FAST) {
+                // block_size >= 64 and a multiple of 16: the tile spans at most
+                // two blocks and no copy straddles a block boundary
                 FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
                 const int b0 = __builtin_amdgcn_readfirstlane((int)fdiv((uint32_t)kbase, fd));
                 const int first = b0 * P.block_size;
-                bnd = first + P.block_size - kbase;
+                const int bnd = first + P.block_size - kbase;   // first in-tile key of block b0+1
                 const bool two = bnd < BN && kbase + bnd < n_keys;
-                const int blk0 = __builtin_amdgcn_readfirstlane((int)bt_at(b0));
-                const int blk1 = __builtin_amdgcn_readfirstlane(two ? (int)bt_at(b0 + 1) : blk0);
-                const int64_t gh = (int64_t)g * P.stride_head;
-                base0 = (blk0 >= 0 && blk0 < P.num_blocks)
-                            ? (int64_t)blk0 * P.stride_block + (int64_t)(kbase - first) * P.stride_tok + gh
-                            : BAD;
-                base1 = (blk1 >= 0 && blk1 < P.num_blocks)
-                            ? (int64_t)blk1 * P.stride_block +
-                                  (int64_t)(kbase - first - P.block_size) * P.stride_tok + gh
-                            : BAD;
-            }
+                // an id outside the pool reads block 0 instead (caller error)
+                int blk0 = bt_scalar(b0);
+                int blk1 = two ? bt_scalar(b0 + 1) : blk0;
+                blk0 = (uint32_t)blk0 < nb32 ? blk0 : 0;
+                blk1 = (uint32_t)blk1 < nb32 ? blk1 : 0;
+                const int64_t off0 = (int64_t)blk0 * sbb + (int64_t)(kbase - first) * stb + ghb;
+                const int64_t off1 = (int64_t)blk1 * sbb + (int64_t)(kbase - first - P.block_size) * stb + ghb;
+                const int nk = n_keys - kbase;
 #pragma unroll
-            for (int i = 0; i < C::K_INSTR_PER_WAVE; ++i) {
-                const int q = wave * C::K_INSTR_PER_WAVE + i;
-                const int row = q * C::KROWS_PER_INSTR + lane / C::KROW_CHUNKS;
-                const int c = pc ^ (row & C::KSWZ);
-                int64_t off = 0;
-                bool ok;
-                if constexpr (FAST) {
-                    const int64_t b = row < bnd ? base0 : base1;
-                    off = b + (int64_t)row * P.stride_tok;
-                    ok = kbase + row < n_keys && b != BAD;
-                } else {
-                    const int key = kbase + row;
-                    ok = key < n_keys;
+                for (int i = 0; i < C::K_PER_WAVE; ++i) {
+                    const int q = wave_u * C::K_PER_WAVE + i;
+                    const int ko = q * C::RPI;
+                    const int64_t off = ko < nk ? (ko < bnd ? off0 : off1) + (int64_t)ko * stb : 0;
+                    dma16(kpool + off + k_lane_src, kl + q * K_COPY_STRIDE);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::K_PER_WAVE; ++i) {
+                    const int q = wave_u * C::K_PER_WAVE + i;
+                    const int key = kbase + q * C::RPI + k_sub;
+                    bool ok = key < n_keys;
+                    int64_t off = 0;
                     if (ok) {
                         FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
                         const uint32_t bi = fdiv((uint32_t)key, fd);
                         const int64_t blk = bt_at((int)bi);   // widened before any product
                         ok = blk >= 0 && blk < P.num_blocks;
-                        off = blk * P.stride_block + (int64_t)(key - (int)bi * P.block_size) * P.stride_tok +
-                              (int64_t)g * P.stride_head;
+                        off = blk * sbb + (int64_t)(key - (int)bi * P.block_size) * stb + ghb;
                     }
+                    dma16(kpool + (ok ? off : 0) + k_chunk * 16, kl + q * K_COPY_STRIDE);
                 }
-                dma16((const __bf16 *)P.k + (ok ? off + c * 8 : 0), kl + q * 1024);
             }
         } else if constexpr (C::K_I8) {
-            const char *img = P.k_img + (img_base + (int64_t)kt * P.Hkv) * image_bytes(D);
+            const char *img = P.k_img + (img_base + (int64_t)kt * P.Hkv) * k_image_bytes(D);
 #pragma unroll
-            for (int i = 0; i < C::K_INSTR_PER_WAVE; ++i) {
-                const int q = wave * C::K_INSTR_PER_WAVE + i;
-                dma16(img + q * 1024 + lane * 16, kl + q * 1024);
+            for (int i = 0; i < C::K_PER_WAVE; ++i) {
+                const int q = wave_u * C::K_PER_WAVE + i;
+                dma16(img + q * 1024 + k_lane_src, kl + q * K_COPY_STRIDE);
             }
-            if (wave == NWAVE - 1) dma4(img + C::K_BYTES + lane * 4, kl + C::K_BYTES);
+            if (wave_u == NWAVE - 2) dma4(img + BN * 2 * D + k_key_lane * 4, kl + C::K_BYTES);
         } else {
+            const char *k8 = (const char *)P.k;
+            const bool full = kbase + BN <= n_keys;
 #pragma unroll
-            for (int i = 0; i < C::K_INSTR_PER_WAVE; ++i) {
-                const int q = wave * C::K_INSTR_PER_WAVE + i;
-                const int row = q * C::KROWS_PER_INSTR + lane / C::KROW_CHUNKS;
-                const int c = pc ^ (row & C::KSWZ);
-                const int key = kbase + row;
-                dma16((const int8_t *)P.k + (key < n_keys ? ((k8_row0 + key) * P.Hkv + g) * D + c * 16 : 0),
-                      kl + q * 1024);
+            for (int i = 0; i < C::K_PER_WAVE; ++i) {
+                const int q = wave_u * C::K_PER_WAVE + i;
+                const int key0 = kbase + q * C::RPI;
+                const char *base = k8 + ((k8_row0 + key0) * P.Hkv + g) * D;
+                if (full) {
+                    dma16(base + k_lane_src, kl + q * K_COPY_STRIDE);
+                } else {
+                    // last tile: rows past the context read the copy's first row
+                    // (or row 0 of the array when the whole copy is past it)
+                    const bool ok = key0 + k_sub < n_keys;
+                    dma16((key0 < n_keys ? base : k8) + (ok ? k_lane_src : (uint32_t)(k_chunk * 16)),
+                          kl + q * K_COPY_STRIDE);
+                }
             }
-            if (wave == NWAVE - 1) {
-                const int key = kbase + lane;
-                dma4(P.kscale + (key < n_keys ? (k8_row0 + key) * P.Hkv + g : 0), kl + C::K_BYTES);
+            if (wave_u == NWAVE - 2) {
+                const int key = kbase + k_key_lane;
+                dma4(P.kscale + (k8_row0 + (key < n_keys ? key : kbase)) * P.Hkv + g, kl + C::K_BYTES);
             }
         }
     };
@@ -286,27 +323,28 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // ---- V^T tile kt (an image built by the V pass) into LDS stage `stage`
     auto dma_v = [&](int kt, int stage) {
         char *vl = vstage(stage);
-        const char *img = P.v_img + (img_base + (int64_t)kt * P.Hkv) * image_bytes(D);
+        const char *img = P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D);
 #pragma unroll
-        for (int i = 0; i < C::V_INSTR_PER_WAVE; ++i) {
-            const int q = wave * C::V_INSTR_PER_WAVE + i;
-            dma16(img + q * 1024 + lane * 16, vl + q * 1024);
+        for (int i = 0; i < C::V_PER_WAVE; ++i) {
+            const int q = i * NWAVE + wave_u;
+            if (C::VCOPIES % NWAVE == 0 || q < C::VCOPIES) dma16(img + q * 1024 + lane * 16, vl + q * 1024);
         }
         if constexpr (C::V_I8) {
-            if (wave == 0) dma4(img + C::V_BYTES + lane * 4, vl + C::V_BYTES);
+            if (wave_u == NWAVE - 1) dma4(img + C::V_BYTES + lane * 4, vl + C::V_BYTES);
         }
     };
+
+    // per-lane operand read bases: K row of MFMA position 32 kb + lc, V^T row lc
+    const int k_rd = K_COPY_STRIDE * (lc % C::KCOPIES) + (lc / C::KCOPIES) * C::K_ROW_BYTES + hf * 16;
+    const int v_rd = lc * VT_ROW_BYTES + hf * 16;
 
     // ---- S^T = K Q^T for the 2 blocks of 32 keys of a K stage (logits in
     // log2 units for the int8-QK arm, raw otherwise); A operands are read two
     // k-steps ahead of the MFMAs that use them
     auto qk_tile = [&](int stage, f32x16 (&s)[2]) {
         const char *kl = kstage(stage);
-        auto rd = [&](int ks, int kb) -> u32x4 {
-            const int row = kb * 32 + lc;
-            const int c = (2 * ks + hf) ^ (row & C::KSWZ);
-            return *(const u32x4 *)(kl + row * C::K_ROW_BYTES + c * 16);
-        };
+        const char *kr = kl + k_rd;
+        auto rd = [&](int ks, int kb) -> u32x4 { return *(const u32x4 *)(kr + kb * C::KB_STEP + ks * 32); };
         constexpr int PF = 2;
         u32x4 a[PF + 1][2];
 #pragma unroll
@@ -381,13 +419,12 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // softmax of one tile's logits, in place: s becomes P (relative to m_run)
     auto softmax_tile = [&](f32x16 (&s)[2], int kt) {
         if (kt * BN + BN - 1 > pos_min) {   // tiles that reach past the first column
+            const int lim = my_pos - kt * BN - hf * C::HSTEP;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kt * BN + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                    if (key > my_pos) s[kb][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) s[kb][i] = -INFINITY;
         }
         float mx = -INFINITY;
 #pragma unroll
@@ -399,10 +436,16 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = exp2_fast(m_run - m_new);
             l_run *= alpha;
+            // the empty asm pins O to the accumulator registers on both sides of
+            // this rare branch, so the copies it needs stay inside it (otherwise
+            // they are hoisted into every iteration)
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+            for (int db = 0; db < C::DB; ++db) {
+                asm volatile("" : "+a"(o[db]));
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                asm volatile("" : "+a"(o[db]));
+            }
             m_run = m_new;
         }
         float psum = 0.f;
@@ -421,11 +464,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // dims; A operands are read PF ahead of the MFMAs that use them
     auto pv_tile = [&](int stage, const f32x16 (&s)[2]) {
         const char *vl = vstage(stage);
+        const char *vr = vl + v_rd;
         auto rd = [&](int i) -> f16x8 {
             const int st = i / C::DB, db = i % C::DB;
-            const int d = db * 32 + lc;
-            const int c = (2 * st + hf) ^ vt_swz(d);
-            return *(const f16x8 *)(vl + d * (BN * 2) + c * 16);
+            return *(const f16x8 *)(vr + db * 32 * VT_ROW_BYTES + st * 32);
         };
         constexpr int NOPS = 4 * C::DB;
         constexpr int PF = 3;
@@ -496,19 +538,27 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         }
 }
 
+template <int D, int KIND, bool FAST>
+static void launch_f(bool out_bf16, const AttnParams &p, dim3 grid, hipStream_t s) {
+    if (out_bf16)
+        hipLaunchKernelGGL((attn_kernel<D, KIND, true, FAST>), grid, dim3(NTHR), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn_kernel<D, KIND, false, FAST>), grid, dim3(NTHR), 0, s, p);
+}
+
 template <int D, int KIND>
 static hipError_t launch_t(bool out_bf16, const AttnParams &p, dim3 grid, hipStream_t s) {
-    const bool fast = p.block_size >= BN;
-    if (out_bf16) {
+    if constexpr (KIND == KIND_BF16) {
+        // scalar-addressed K copies: blocks of >= 64 keys in whole multiples of
+        // 16, and a copy's per-lane offsets within 32 bits
+        const bool fast = p.block_size >= BN && p.block_size % 16 == 0 &&
+                          15 * p.stride_tok * 2 + 2 * D < ((int64_t)1 << 31);
         if (fast)
-            hipLaunchKernelGGL((attn_kernel<D, KIND, true, true>), grid, dim3(NTHR), 0, s, p);
+            launch_f<D, KIND, true>(out_bf16, p, grid, s);
         else
-            hipLaunchKernelGGL((attn_kernel<D, KIND, true, false>), grid, dim3(NTHR), 0, s, p);
+            launch_f<D, KIND, false>(out_bf16, p, grid, s);
     } else {
-        if (fast)
-            hipLaunchKernelGGL((attn_kernel<D, KIND, false, true>), grid, dim3(NTHR), 0, s, p);
-        else
-            hipLaunchKernelGGL((attn_kernel<D, KIND, false, false>), grid, dim3(NTHR), 0, s, p);
+        launch_f<D, KIND, false>(out_bf16, p, grid, s);   // FAST only shapes paged K
     }
     return hipGetLastError();
 }
@@ -522,6 +572,11 @@ static hipError_t launch_d(int head_dim, bool out_bf16, const AttnParams &p, dim
         case 256: return launch_t<256, KIND>(out_bf16, p, grid, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+int attn_rows_per_copy(int kind, int head_dim) {
+    const bool qk8 = kind == KIND_QK8_VBF16 || kind == KIND_QK8_VI8;
+    return 1024 / (qk8 ? head_dim : 2 * head_dim);
 }
 
 hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,

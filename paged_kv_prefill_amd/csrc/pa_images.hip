@@ -46,26 +46,29 @@ __device__ __forceinline__ bool img_tile(const ImageParams &P, int &t, int &g, i
     return t * TILE_KEYS < L;
 }
 
-// V^T image: [D][64] fp16 + 64 scales.  One unit = 4 consecutive keys x one
-// 16-byte chunk of the source row; its 4 x 8 (bf16) or 4 x 16 (int8) values are
-// written to LDS as 8-byte groups of 4 keys of one dim.
+// V^T image: [D][72] fp16 (64 columns in MFMA-position order + zero padding)
+// + 64 scales in position order.  One unit = 4 consecutive positions (4
+// consecutive columns) x one 16-byte chunk of the source row; its 4 x 8 (bf16)
+// or 4 x 16 (int8) values go to LDS as 8-byte groups of the 4 columns of one dim.
 template <int D, bool SRC_I8>
 __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
     constexpr int CPR = (SRC_I8 ? D : 2 * D) / 16;
     constexpr int UNITS = 16 * CPR;
-    constexpr int V_BYTES = TILE_KEYS * D * 2;
+    constexpr int V_BYTES = vt_tile_bytes(D);
     __shared__ __attribute__((aligned(16))) char img[V_BYTES + TILE_KEYS * 4];
     int t, g, r, L;
     if (!img_tile(P, t, g, r, L)) return;
     const int tid = threadIdx.x;
+    const int rpi = P.v_rpi;
     float *scl = (float *)(img + V_BYTES);
+    for (int d = tid; d < D; d += IT) *(u32x4 *)(img + d * VT_ROW_BYTES + TILE_KEYS * 2) = u32x4{0, 0, 0, 0};
     for (int u = tid; u < UNITS; u += IT) {
-        const int dc = u % CPR, kg = u / CPR;
+        const int dc = u % CPR, pg = u / CPR;
         u32x4 w[4];
         float s[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int key = t * TILE_KEYS + kg * 4 + j;
+            const int key = t * TILE_KEYS + tile_key(pg * 4 + j, rpi);
             int64_t off = 0, soff = 0;
             const bool ok = key < L && img_row(P, r, key, g, off, soff);
             if (SRC_I8) {
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
                 s[j] = 0.f;
             }
         }
-        const int slot = vt_slot(kg * 4);
+        const int slot = vt_slot(pg * 4);
         if (SRC_I8) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -98,24 +101,23 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
         }
         if (dc == 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) scl[kg * 4 + j] = s[j];
+            for (int j = 0; j < 4; ++j) scl[pg * 4 + j] = s[j];
         }
     }
     __syncthreads();
-    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * image_bytes(D);
+    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * v_image_bytes(D);
     constexpr int CHUNKS = (V_BYTES + TILE_KEYS * 4) / 16;
     for (int c = tid; c < CHUNKS; c += IT) *(u32x4 *)(dst + c * 16) = *(const u32x4 *)(img + c * 16);
 }
 
-// K image of an int8 pool: [64][D] bf16 codes (exact), XOR-swizzled chunks, + 64 scales.
+// K image of an int8 pool: [64][D] bf16 codes (exact) in key order + 64 scales.
 template <int D>
 __global__ __launch_bounds__(IT) void k_image_kernel(const ImageParams P) {
     constexpr int CPR = D / 16;                      // source chunks (16 codes) per row
-    constexpr int KSWZ = ktile_swz_mask(2 * D);
     int t, g, r, L;
     if (!img_tile(P, t, g, r, L)) return;
     const int tid = threadIdx.x;
-    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * image_bytes(D);
+    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * k_image_bytes(D);
     float *scl = (float *)(dst + TILE_KEYS * D * 2);
     for (int u = tid; u < TILE_KEYS * CPR; u += IT) {
         const int row = u / CPR, dc = u % CPR;
@@ -133,8 +135,7 @@ __global__ __launch_bounds__(IT) void k_image_kernel(const ImageParams P) {
                 o[q] = pack_bf16x2((float)(int8_t)((word >> sh) & 0xff),
                                    (float)(int8_t)((word >> (sh + 8)) & 0xff));
             }
-            const int c = (dc * 2 + half) ^ (row & KSWZ);
-            *(u32x4 *)(dst + row * (D * 2) + c * 16) = o;
+            *(u32x4 *)(dst + row * (D * 2) + (dc * 2 + half) * 16) = o;
         }
         if (dc == 0) scl[row] = ok ? P.src_scales[soff] : 0.f;
     }

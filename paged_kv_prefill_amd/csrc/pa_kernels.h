@@ -73,6 +73,7 @@ struct ImageParams {
     int64_t stride_block, stride_tok, stride_head;
     int64_t stride_sblock, stride_stok;
     int64_t tiles;              // T: tiles per request
+    int32_t v_rpi;              // key rows per 1 KB K copy of the consuming attention kernel
     const void *src;            // V pool
     const float *src_scales;    // V scales (int8 pool)
     const void *src2;           // K pool (int8 exact arm)
@@ -84,6 +85,8 @@ struct ImageParams {
 // launchers: return hipError_t of the launch
 hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,
                             int32_t max_q_len, hipStream_t stream);
+// key rows per 1 KB K copy of an attention kind (fixes the tile's key order)
+int attn_rows_per_copy(int kind, int head_dim);
 hipError_t launch_images(const ImageParams &p, bool v_int8, bool k_image, hipStream_t stream);
 hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);
 hipError_t launch_k_quant(const PassParams &p, hipStream_t stream);

@@ -3,32 +3,51 @@
 //
 // A KV tile holds 64 consecutive key positions of one (request, KV head).
 //
-// K tile (bf16, or int8 for the int8-QK arm): row-major [64][D]; the 16-byte
-// chunk c of row r is stored at chunk c ^ (r & kswz), kswz = min(chunks, 16) - 1,
-// so that 16 consecutive rows read at the same logical chunk hit 16 distinct
-// chunk slots (64 LDS banks).
+// K tile (bf16 codes/values, or int8 for the int8-QK arm), rows of R bytes.
+// It arrives as 64 / rpi direct copies of 1 KB (rpi = 1024 / R consecutive
+// keys each, so each copy reads from one cache block); copy q lands at LDS
+// byte q * 1040, i.e. 16 bytes of padding per KB: consecutive copies start 4
+// banks apart.  The MFMA's 32-row A operand does not take the keys in order:
+// row i of key block kb holds key tile_key(32 kb + i), chosen so that the 16
+// lanes of one LDS read phase hit 16 different 4-bank groups and every operand
+// read of a lane is its own base plus a compile-time offset.
 //
-// V^T tile (fp16): [D][64]; within each group of 16 keys, keys {0-3, 8-11}
-// take slots 0-7 and {4-7, 12-15} take slots 8-15 (the key order in which
-// the S accumulator rows reach the PV MFMA), and the 16-byte chunk c of row d
-// is stored at c ^ ((d ^ (d >> 3)) & 7).
+// V^T tile (fp16): [D][64 + 8 pad] (144-byte rows, 36 dwords: 16 consecutive
+// rows fall on 16 disjoint 4-bank groups).  Its 64 columns follow the MFMA
+// positions of the K tile (column of position p holds key tile_key(p)), with
+// positions {0-3, 8-11} of each group of 16 in columns 0-7 and {4-7, 12-15} in
+// columns 8-15: the order in which the S accumulator rows reach the PV MFMA,
+// so each PV operand is one 16-byte read.
 //
-// Tile images in global memory (the workspace) are byte-for-byte copies of
-// these LDS tiles, followed by 64 fp32 per-key scales, so a workgroup moves a
-// tile with straight 1 KB direct-to-LDS copies.
+// V^T images in global memory (the workspace) are byte-for-byte copies of the
+// LDS tile followed by 64 fp32 per-key scales in position order (int8 V), so
+// a workgroup moves them with straight 1 KB direct-to-LDS copies.  K images
+// (int8-KV exact arm) hold [64][D] bf16 codes in key order (the 1 KB copies
+// re-space them) followed by 64 fp32 per-key scales in key order.
 #pragma once
 #include <stdint.h>
 
 namespace pa {
 
 constexpr int TILE_KEYS = 64;
+constexpr int VT_ROW_BYTES = TILE_KEYS * 2 + 16;   // one padded V^T row (fp16)
 
-__host__ __device__ constexpr int ktile_swz_mask(int row_bytes) {
-    return (row_bytes / 16 < 16 ? row_bytes / 16 : 16) - 1;
+constexpr int K_COPY_STRIDE = 1024 + 16;          // LDS bytes per 1 KB K copy
+
+// key (0..63) held at MFMA position p = 32 * kb + i of a K tile whose rows are
+// copied rpi at a time (rpi in {2, 4, 8, 16})
+__host__ __device__ constexpr int tile_key(int p, int rpi) {
+    const int g = 64 / rpi, kb = p >> 5, i = p & 31;
+    return rpi * (i % g) + i / g + (32 / g) * kb;
 }
 
-// bytes of one tile image (tile + 64 fp32 scales)
-__host__ __device__ constexpr int64_t image_bytes(int head_dim) {
+// bytes of one V^T tile in LDS and of one V^T image (tile + 64 fp32 scales)
+__host__ __device__ constexpr int vt_tile_bytes(int head_dim) { return head_dim * VT_ROW_BYTES; }
+__host__ __device__ constexpr int64_t v_image_bytes(int head_dim) {
+    return (int64_t)vt_tile_bytes(head_dim) + TILE_KEYS * 4;
+}
+// bytes of one K image (int8-KV exact arm): 64 rows of bf16 codes + 64 scales
+__host__ __device__ constexpr int64_t k_image_bytes(int head_dim) {
     return (int64_t)TILE_KEYS * head_dim * 2 + TILE_KEYS * 4;
 }
 
@@ -36,15 +55,12 @@ __host__ __device__ inline int64_t tiles_per_request(int32_t max_ctx_len) {
     return ((int64_t)max_ctx_len + TILE_KEYS - 1) / TILE_KEYS;
 }
 
-// slot of key k (0..63) in a row of the V^T tile
-__host__ __device__ inline int vt_slot(int k) {
-    const int k16 = k & 15;
-    return (k & ~15) | (k16 & 3) | ((k16 >> 3) << 2) | (((k16 >> 2) & 1) << 3);
+// column of MFMA position p (0..63) in a row of the V^T tile (swaps bits 2 and 3)
+__host__ __device__ inline int vt_slot(int p) {
+    const int k16 = p & 15;
+    return (p & ~15) | (k16 & 3) | ((k16 >> 3) << 2) | (((k16 >> 2) & 1) << 3);
 }
-__host__ __device__ inline int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-// byte offset of (d, slot) in a [D][64] fp16 V^T tile (8 chunks of 16 B per row)
-__host__ __device__ inline int vt_off(int d, int slot) {
-    return d * (TILE_KEYS * 2) + ((((slot >> 3) ^ vt_swz(d)) << 4) | ((slot & 7) << 1));
-}
+// byte offset of (d, slot) in a V^T tile
+__host__ __device__ inline int vt_off(int d, int slot) { return d * VT_ROW_BYTES + slot * 2; }
 
 }  // namespace pa

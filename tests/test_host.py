@@ -95,13 +95,17 @@ def test_entry_point_specific_errors():
 
 
 def test_workspace_size_formula():
-    """num_reqs * ceil(max_ctx / 64) * Hkv images of 128 * D + 256 bytes."""
+    """num_reqs * ceil(max_ctx / 64) * Hkv V^T images of 144 * D + 256 bytes
+    (fp16 rows of 64 keys padded to 72), plus as many K images of 128 * D + 256
+    bytes for the int8-KV exact arm."""
     L = ops.lib()
     a = _args(num_reqs=3, max_ctx_len=130, num_kv_heads=2, head_dim=64)
-    img = 128 * 64 + 256
-    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_BF16) == 3 * 3 * 2 * img
-    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8QK) == 3 * 3 * 2 * img
-    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8KV) == 2 * 3 * 3 * 2 * img
+    vimg = 144 * 64 + 256
+    kimg = 128 * 64 + 256
+    n = 3 * 3 * 2
+    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_BF16) == n * vimg
+    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8QK) == n * vimg
+    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8KV) == n * (vimg + kimg)
     assert L.pa_workspace_bytes(C.byref(a), 99) == 0
     assert L.pa_workspace_bytes(C.byref(_args(num_q_heads=3)), ops.PA_ENTRY_PREFILL_BF16) == 0
 
