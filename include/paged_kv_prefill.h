@@ -160,6 +160,8 @@ int pa_k_quant(const pa_paged_args *args, const void *k_pool, int32_t k_dtype,
  * then fp32 online softmax and bf16 PV.
  *   k8, ks     outputs of pa_k_quant / pa_k_stats, indexed by position
  *   v_pool     v_dtype PA_DTYPE_BF16 (bf16 pool) or PA_DTYPE_INT8 (codes, with v_scales)
+ * PA_ERR_TOO_LARGE if max_ctx_len * num_kv_heads * head_dim >= 2^31 (one
+ * request's k8 rows are addressed with 32-bit offsets).
  */
 int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8,
                       const float *ks, const int32_t *cu_ctx, const void *v_pool,

@@ -251,6 +251,8 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     if (!k8 || !ks || !cu_ctx || !v_pool) return PA_ERR_NULL;
     if (v_dtype == PA_DTYPE_INT8 && (rc = check_scales(a, v_scales))) return rc;
     if (!aligned16(k8) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    // a request's k8 rows and ks entries are addressed with 32-bit offsets
+    if ((int64_t)a->max_ctx_len * a->num_kv_heads * a->head_dim >= ((int64_t)1 << 31)) return PA_ERR_TOO_LARGE;
     if ((rc = check_workspace(a, PA_ENTRY_PREFILL_INT8QK, workspace, workspace_bytes))) return rc;
     const int kind = v_dtype == PA_DTYPE_INT8 ? KIND_QK8_VI8 : KIND_QK8_VBF16;
     ImageParams ip = image_params(a, workspace, kind);

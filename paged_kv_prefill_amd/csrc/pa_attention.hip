@@ -32,7 +32,7 @@
 // instruction, no registers).  A K copy takes the rows of 1024 / R consecutive
 // keys (R = bytes per key row); with block_size a multiple of 16 those keys
 // sit in one cache block, so the copy's address is a wave-uniform scalar (block
-// id from the block-table row cached in LDS, widened to 64 bits) plus a
+// id read through the scalar cache, widened to 64 bits) plus a
 // per-lane constant, and the loop spends no vector instructions on it.  V comes
 // from the per-tile V^T images that pa_images.hip builds once per call.  The
 // tile layouts (pa_layout.h) pad rows instead of swizzling them, so every
@@ -51,6 +51,8 @@
 // the logits are scaled per key afterwards, and the V^T tile holds codes for
 // the fp16 PV MFMA with each key's V scale folded into P.  No dequantised
 // value is ever rounded.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 #include "pa_layout.h"
@@ -63,6 +65,16 @@ constexpr int NTHR = 64 * NWAVE;
 constexpr int NCOL = 32 * NWAVE;
 constexpr int LDS_MAX = 160 * 1024;
 constexpr float RESCALE_SLACK = 8.0f;   // lazy-rescale threshold, log2 units
+#ifndef PA_QK_AHEAD
+#define PA_QK_AHEAD 8
+#endif
+#ifndef PA_PV_AHEAD
+#define PA_PV_AHEAD 6
+#endif
+// LDS operand reads are issued this many MFMAs ahead of the MFMA that uses them
+constexpr int QK_AHEAD = PA_QK_AHEAD;
+constexpr int PV_AHEAD = PA_PV_AHEAD;
+#define PA_FENCE() __builtin_amdgcn_sched_barrier(0)
 static_assert(NTHR == ATTN_THREADS && NCOL == ATTN_COLS, "launch geometry");
 
 template <int D, int KIND>
@@ -82,6 +94,7 @@ struct AttnCfg {
     static constexpr int KSTAGE = K_BYTES + (K_SCALED ? BN * 4 : 0);
     static constexpr int VSTAGE = V_BYTES + (V_I8 ? BN * 4 : 0);
     static constexpr int BT_OFF = 2 * KSTAGE + 2 * VSTAGE;
+    // block-table entries cached in LDS by the FAST paged path
     static constexpr int BT_CAP = K_PAGED ? ((LDS_MAX - BT_OFF) / 4 < 4096 ? (LDS_MAX - BT_OFF) / 4 : 4096) : 0;
     static constexpr int LDS = BT_OFF + BT_CAP * 4;
     static constexpr int K_PER_WAVE = KCOPIES / NWAVE;
@@ -106,14 +119,28 @@ __host__ __device__ constexpr bool hstep_uniform(int rpi) {
 }
 static_assert(hstep_uniform(2) && hstep_uniform(4) && hstep_uniform(8) && hstep_uniform(16), "HSTEP");
 
-__device__ __forceinline__ void dma16(const void *src, char *lds) {
+// Direct global-to-LDS copies.  The buffer form (buffer_load_dwordx4 ... lds)
+// is used wherever the source has a wave-uniform base: the LDS destination is
+// the given pointer + 16 (or 4) bytes per lane, the source is base + voffset
+// (per lane) + soffset (uniform).  The flat/global form is kept for per-lane
+// 64-bit addresses only: the compiler's wait-count tracking then treats every
+// later LDS read as unordered and waits for all of them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void *base) {
+    // raw buffer, stride 0, no range limit that any offset here can reach
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void gdma16(const void *src, char *lds) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void *src, char *lds) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
-}
 
-// FAST: block_size >= 64 (a tile spans at most two blocks), chosen on the host.
+// FAST (paged K only, chosen on the host): block_size a multiple of 16, so no
+// K copy straddles a block, and the block-table row fits the LDS cache.
 template <int D, int KIND, bool OUT_BF16, bool FAST>
 __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     using C = AttnCfg<D, KIND>;
@@ -205,21 +232,15 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         lfac = sq * P.scale_log2;
     }
 
-    // ---- block-table row of this request, cached in LDS (paged K only)
-    int32_t *bt_lds = (int32_t *)(smem + C::BT_OFF);
+    // ---- block-table row of this request; the FAST paged path keeps it in LDS
+    // and reads wave-uniform entries from there
     const int64_t bt_row = (int64_t)r * P.stride_bt;
-    if constexpr (C::K_PAGED) {
-        const int n_blk = (n_keys - 1) / P.block_size + 1;
-        for (int i = tid; i < n_blk && i < C::BT_CAP; i += NTHR) bt_lds[i] = P.bt[bt_row + i];
+    int32_t *bt_lds = (int32_t *)(smem + C::BT_OFF);
+    if constexpr (C::K_PAGED && FAST) {
+        const int n_blk = (n_keys - 1) / P.block_size + 1;   // at most BT_CAP (host check)
+        for (int i = tid; i < n_blk; i += NTHR) bt_lds[i] = P.bt[bt_row + i];
         __syncthreads();
     }
-    auto bt_at = [&](int i) -> int64_t {
-        return (int64_t)(i < C::BT_CAP ? bt_lds[i] : P.bt[bt_row + i]);
-    };
-    // wave-uniform block-table entry through the scalar cache (read only)
-    auto bt_scalar = [&](int i) -> int {
-        return ((const __attribute__((address_space(4))) int32_t *)P.bt)[bt_row + i];
-    };
 
     const int64_t img_base = ((int64_t)r * P.img_tiles) * P.Hkv + g;   // image index of tile 0
     const int64_t k8_row0 = C::QK8 ? (int64_t)P.cu_ctx[r] : 0;
@@ -239,99 +260,107 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     else k_lane_src = (uint32_t)(lane * 16);
     const int k_key_lane = tile_key(lane, C::RPI);                     // key of scale slot `lane`
 
-    // ---- K tile kt into LDS stage `stage`: copy q (keys q*rpi ...) lands at
-    // q * K_COPY_STRIDE.  Keys past the context read a mapped dummy row; their
-    // logits are masked.
-    auto dma_k = [&](int kt, int stage) {
+    // ---- K tile kt into LDS stage `stage`, as NKC copy instructions per wave:
+    // copy q (keys q*rpi ...) lands at q * K_COPY_STRIDE; the last one carries
+    // the per-key scales where the tile has them.  k_src computes the tile's
+    // wave-uniform source once; k_copy issues one instruction, so a step can
+    // spread its copies between its MFMAs.  Keys past the context read a mapped
+    // dummy row; their logits are masked.
+    struct KSrc {
+        __amdgpu_buffer_rsrc_t rs;
+        uint32_t soff;
+    };
+    auto k_src = [&](int kt) -> KSrc {
+        const int kbase = kt * BN;
+        if constexpr (C::K_PAGED && FAST) {
+            // a wave's copies cover 16 consecutive keys, so one cache block; a
+            // wave whose keys are all past the context re-reads the last 16
+            // inside it
+            FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
+            const int kw = min(kbase + wave_u * 16, (n_keys - 1) & ~15);
+            const int b = (int)fdiv((uint32_t)kw, fd);
+            int id = __builtin_amdgcn_readfirstlane(bt_lds[b]);
+            id = (uint32_t)id < nb32 ? id : 0;   // an id outside the pool reads block 0 (caller error)
+            return KSrc{rsrc_at((const char *)P.k + (int64_t)id * sbb + ghb),
+                        (uint32_t)((kw - b * P.block_size) * stb)};
+        } else if constexpr (C::K_I8) {
+            return KSrc{rsrc_at(P.k_img + (img_base + (int64_t)kt * P.Hkv) * k_image_bytes(D)), 0u};
+        } else if constexpr (C::QK8) {
+            // dense k8 rows of this request: [cu_ctx[r] + key][Hkv][D]
+            return KSrc{rsrc_at((const char *)P.k + (k8_row0 * P.Hkv + g) * D), 0u};
+        } else {
+            return KSrc{rsrc_at(P.k), 0u};   // per-lane addresses below
+        }
+    };
+    auto k_copy = [&](const KSrc &src, int kt, int stage, int i) {
         char *kl = kstage(stage);
         const int kbase = kt * BN;
-        if constexpr (C::K_PAGED) {
-            const char *kpool = (const char *)P.k;
-            if constexpr (FAST) {
-                // block_size >= 64 and a multiple of 16: the tile spans at most
-                // two blocks and no copy straddles a block boundary
+        if (i == C::K_PER_WAVE) {   // per-key scales
+            if constexpr (C::K_I8) {
+                if (wave_u == NWAVE - 2) bdma4(src.rs, k_key_lane * 4, BN * 2 * D, kl + C::K_BYTES);
+            } else if constexpr (C::QK8) {
+                if (wave_u == NWAVE - 2) {
+                    const int key = kbase + k_key_lane;
+                    const auto ks = rsrc_at(P.kscale + k8_row0 * P.Hkv + g);
+                    bdma4(ks, (uint32_t)((key < n_keys ? key : 0) * P.Hkv * 4), 0, kl + C::K_BYTES);
+                }
+            }
+            return;
+        }
+        const int q = wave_u * C::K_PER_WAVE + i;
+        char *dst = kl + q * K_COPY_STRIDE;
+        if constexpr (C::K_PAGED && FAST) {
+            bdma16(src.rs, k_lane_src, src.soff + (uint32_t)(i * C::RPI * stb), dst);
+        } else if constexpr (C::K_PAGED) {
+            const int key = kbase + q * C::RPI + k_sub;
+            bool ok = key < n_keys;
+            int64_t off = 0;
+            if (ok) {
                 FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
-                const int b0 = __builtin_amdgcn_readfirstlane((int)fdiv((uint32_t)kbase, fd));
-                const int first = b0 * P.block_size;
-                const int bnd = first + P.block_size - kbase;   // first in-tile key of block b0+1
-                const bool two = bnd < BN && kbase + bnd < n_keys;
-                // an id outside the pool reads block 0 instead (caller error)
-                int blk0 = bt_scalar(b0);
-                int blk1 = two ? bt_scalar(b0 + 1) : blk0;
-                blk0 = (uint32_t)blk0 < nb32 ? blk0 : 0;
-                blk1 = (uint32_t)blk1 < nb32 ? blk1 : 0;
-                const int64_t off0 = (int64_t)blk0 * sbb + (int64_t)(kbase - first) * stb + ghb;
-                const int64_t off1 = (int64_t)blk1 * sbb + (int64_t)(kbase - first - P.block_size) * stb + ghb;
-                const int nk = n_keys - kbase;
-#pragma unroll
-                for (int i = 0; i < C::K_PER_WAVE; ++i) {
-                    const int q = wave_u * C::K_PER_WAVE + i;
-                    const int ko = q * C::RPI;
-                    const int64_t off = ko < nk ? (ko < bnd ? off0 : off1) + (int64_t)ko * stb : 0;
-                    dma16(kpool + off + k_lane_src, kl + q * K_COPY_STRIDE);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < C::K_PER_WAVE; ++i) {
-                    const int q = wave_u * C::K_PER_WAVE + i;
-                    const int key = kbase + q * C::RPI + k_sub;
-                    bool ok = key < n_keys;
-                    int64_t off = 0;
-                    if (ok) {
-                        FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
-                        const uint32_t bi = fdiv((uint32_t)key, fd);
-                        const int64_t blk = bt_at((int)bi);   // widened before any product
-                        ok = blk >= 0 && blk < P.num_blocks;
-                        off = blk * sbb + (int64_t)(key - (int)bi * P.block_size) * stb + ghb;
-                    }
-                    dma16(kpool + (ok ? off : 0) + k_chunk * 16, kl + q * K_COPY_STRIDE);
-                }
+                const uint32_t bi = fdiv((uint32_t)key, fd);
+                const int64_t blk = P.bt[bt_row + bi];   // widened before any product
+                ok = blk >= 0 && blk < P.num_blocks;
+                off = blk * sbb + (int64_t)(key - (int)bi * P.block_size) * stb + ghb;
             }
+            gdma16((const char *)P.k + (ok ? off : 0) + k_chunk * 16, dst);
         } else if constexpr (C::K_I8) {
-            const char *img = P.k_img + (img_base + (int64_t)kt * P.Hkv) * k_image_bytes(D);
-#pragma unroll
-            for (int i = 0; i < C::K_PER_WAVE; ++i) {
-                const int q = wave_u * C::K_PER_WAVE + i;
-                dma16(img + q * 1024 + k_lane_src, kl + q * K_COPY_STRIDE);
-            }
-            if (wave_u == NWAVE - 2) dma4(img + BN * 2 * D + k_key_lane * 4, kl + C::K_BYTES);
+            bdma16(src.rs, k_lane_src, q * 1024, dst);
         } else {
-            const char *k8 = (const char *)P.k;
-            const bool full = kbase + BN <= n_keys;
-#pragma unroll
-            for (int i = 0; i < C::K_PER_WAVE; ++i) {
-                const int q = wave_u * C::K_PER_WAVE + i;
-                const int key0 = kbase + q * C::RPI;
-                const char *base = k8 + ((k8_row0 + key0) * P.Hkv + g) * D;
-                if (full) {
-                    dma16(base + k_lane_src, kl + q * K_COPY_STRIDE);
-                } else {
-                    // last tile: rows past the context read the copy's first row
-                    // (or row 0 of the array when the whole copy is past it)
-                    const bool ok = key0 + k_sub < n_keys;
-                    dma16((key0 < n_keys ? base : k8) + (ok ? k_lane_src : (uint32_t)(k_chunk * 16)),
-                          kl + q * K_COPY_STRIDE);
-                }
-            }
-            if (wave_u == NWAVE - 2) {
-                const int key = kbase + k_key_lane;
-                dma4(P.kscale + (k8_row0 + (key < n_keys ? key : kbase)) * P.Hkv + g, kl + C::K_BYTES);
+            const int key0 = kbase + q * C::RPI;
+            if (kbase + BN <= n_keys) {
+                bdma16(src.rs, k_lane_src, (uint32_t)(key0 * k8_rowb), dst);
+            } else {
+                // last tile: rows past the context read the request's row 0
+                const bool ok = key0 + k_sub < n_keys;
+                bdma16(src.rs, ok ? (uint32_t)(key0 * k8_rowb) + k_lane_src : (uint32_t)(k_chunk * 16), 0, dst);
             }
         }
     };
+    constexpr int NKC = C::K_PER_WAVE + (C::K_SCALED ? 1 : 0);   // K copy instructions per wave
+    auto dma_k = [&](int kt, int stage) {
+        const KSrc src = k_src(kt);
+#pragma unroll
+        for (int i = 0; i < NKC; ++i) k_copy(src, kt, stage, i);
+    };
 
     // ---- V^T tile kt (an image built by the V pass) into LDS stage `stage`
-    auto dma_v = [&](int kt, int stage) {
+    auto v_src = [&](int kt) { return rsrc_at(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D)); };
+    auto v_copy = [&](__amdgpu_buffer_rsrc_t img, int stage, int i) {
         char *vl = vstage(stage);
-        const char *img = P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D);
+        if (i == C::V_PER_WAVE) {   // per-key scales
+            if constexpr (C::V_I8) {
+                if (wave_u == NWAVE - 1) bdma4(img, lane * 4, C::V_BYTES, vl + C::V_BYTES);
+            }
+            return;
+        }
+        const int q = i * NWAVE + wave_u;
+        if (C::VCOPIES % NWAVE == 0 || q < C::VCOPIES) bdma16(img, lane * 16, q * 1024, vl + q * 1024);
+    };
+    constexpr int NVC = C::V_PER_WAVE + (C::V_I8 ? 1 : 0);       // V copy instructions per wave
+    auto dma_v = [&](int kt, int stage) {
+        const auto img = v_src(kt);
 #pragma unroll
-        for (int i = 0; i < C::V_PER_WAVE; ++i) {
-            const int q = i * NWAVE + wave_u;
-            if (C::VCOPIES % NWAVE == 0 || q < C::VCOPIES) dma16(img + q * 1024 + lane * 16, vl + q * 1024);
-        }
-        if constexpr (C::V_I8) {
-            if (wave_u == NWAVE - 1) dma4(img + C::V_BYTES + lane * 4, vl + C::V_BYTES);
-        }
+        for (int i = 0; i < NVC; ++i) v_copy(img, stage, i);
     };
 
     // per-lane operand read bases: K row of MFMA position 32 kb + lc, V^T row lc
@@ -345,7 +374,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         const char *kl = kstage(stage);
         const char *kr = kl + k_rd;
         auto rd = [&](int ks, int kb) -> u32x4 { return *(const u32x4 *)(kr + kb * C::KB_STEP + ks * 32); };
-        constexpr int PF = 2;
+        constexpr int PF = 2 < C::KSTEPS ? 2 : C::KSTEPS;
         u32x4 a[PF + 1][2];
 #pragma unroll
         for (int i = 0; i < PF && i < C::KSTEPS; ++i) {
@@ -416,22 +445,28 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     float m_run = -INFINITY;   // running (lazy) max of the log2-domain logits
     float l_run = 0.f;         // this half-wave's share of the running sum
 
-    // softmax of one tile's logits, in place: s becomes P (relative to m_run)
-    auto softmax_tile = [&](f32x16 (&s)[2], int kt) {
-        if (kt * BN + BN - 1 > pos_min) {   // tiles that reach past the first column
-            const int lim = my_pos - kt * BN - hf * C::HSTEP;
+    // causal / context mask of tile kt's logits (tiles that reach past the
+    // workgroup's first column only)
+    auto mask_tile = [&](f32x16 (&s)[2], int kt) {
+        const int lim = my_pos - kt * BN - hf * C::HSTEP;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) s[kb][i] = -INFINITY;
-        }
+            for (int i = 0; i < 16; ++i)
+                if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) s[kb][i] = -INFINITY;
+    };
+    // column maximum of a tile's logits, log2 units
+    auto tile_max = [&](const f32x16 (&s)[2]) -> float {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = max_halves(mx) * smfac;
+        return max_halves(mx) * smfac;
+    };
+    // lazy online-softmax update: move the reference maximum (and rescale O
+    // and the row sum) only when some column's maximum grew past the slack
+    auto rescale = [&](float mx) {
         if (__any(mx > m_run + RESCALE_SLACK)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = exp2_fast(m_run - m_new);
@@ -448,74 +483,201 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             }
             m_run = m_new;
         }
+    };
+    // ---- main loop, software-pipelined by one tile: step kt turns tile kt's
+    // logits into P and adds P V(kt) into O while the QK MFMAs of tile kt+1
+    // run, so the softmax's vector work overlaps matrix-core work.  K runs one
+    // tile ahead of V: during step kt the LDS holds K(kt+1) and V(kt) and the
+    // copies of K(kt+2) and V(kt+1) stream into the other stages.
+    const int t_mask = (pos_min + 1) / BN;   // first tile that needs masking
+    f32x16 sa[2], sb[2];
+    dma_k(0, 0);
+    dma_v(0, 0);
+    if (n_tiles > 1) dma_k(1, 1);
+    __syncthreads();
+    qk_tile(0, sa);
+    if (t_mask == 0) mask_tile(sa, 0);
+    float mx = tile_max(sa);
+    __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
+
+    // ---- one pipelined step as a fixed sequence of slots.  Phase A: the QK
+    // MFMAs of tile kt+1, each slot carrying one LDS operand read for a later
+    // MFMA and a share of tile kt's exponentials; phase B: the PV MFMAs of
+    // tile kt, each slot carrying one V read and a share of tile kt+1's
+    // post-processing (scale, mask, running maximum).  Scheduling fences
+    // between slots keep the reads QK_AHEAD / PV_AHEAD MFMAs ahead of their use
+    // and the vector work between matrix instructions.
+    constexpr int NQ = 2 * C::KSTEPS;                  // QK MFMAs per tile
+    constexpr int NP = 4 * C::DB;                      // PV MFMAs per tile
+    constexpr int PFQ = QK_AHEAD < NQ ? QK_AHEAD : NQ;
+    constexpr int PFV = PV_AHEAD < NP ? PV_AHEAD : NP;
+    constexpr int VA = PFQ < PFV ? PFQ : PFV;          // V reads issued in phase A
+    constexpr int MB0 = NP > 4 ? 2 : 0;                // first phase-B slot touching S(kt+1)
+    auto rdK = [&](const char *kr, int m) -> u32x4 {
+        return *(const u32x4 *)(kr + (m & 1) * C::KB_STEP + (m >> 1) * 32);
+    };
+    auto rdV = [&](const char *vr, int n) -> f16x8 {
+        return *(const f16x8 *)(vr + (n % C::DB) * 32 * VT_ROW_BYTES + (n / C::DB) * 32);
+    };
+
+    // HAS_NEXT: tile kt+1 exists; MASK_NEXT: it needs masking
+    auto step = [&](int kt, int cur, f32x16 (&sc)[2], f32x16 (&sn)[2], auto has_next, auto mask_next) {
+        constexpr bool NEXT = decltype(has_next)::value;
+        constexpr bool MASK = decltype(mask_next)::value;
+        const char *kl = kstage(cur ^ 1);
+        const char *kr = kl + k_rd;
+        const char *vl = vstage(cur);
+        const char *vr = vl + v_rd;
+        // copies of K(kt+2) and V(kt+1), one every other slot from the start of
+        // phase A (a tile index past the end re-copies the last tile into a stage
+        // nobody reads again, which keeps the slots branch-free)
+        const int tk = min(kt + 2, n_tiles - 1), tv = min(kt + 1, n_tiles - 1);
+        const KSrc ksrc = k_src(tk);
+        const auto vsrc = v_src(tv);
+        auto copy_slot = [&](int slot) {
+            if (slot % 2 == 0) {
+                const int c = slot / 2;
+                if (c < NKC) k_copy(ksrc, tk, cur, c);
+                else if (c - NKC < NVC) v_copy(vsrc, cur ^ 1, c - NKC);
+            }
+        };
+        u32x4 ka[NQ];
+        f16x8 va[NP];
+        f32x4 vsc[4][2];
+        f32x4 ksc[2][4];
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int m = 0; m < PFQ; ++m) ka[m] = rdK(kr, m);
+        } else {
+#pragma unroll
+            for (int n = 0; n < PFV; ++n) va[n] = rdV(vr, n);
+        }
+        if constexpr (C::V_I8) {
+            const float *vs = (const float *)(vl + C::V_BYTES);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                vsc[st][0] = *(const f32x4 *)(vs + 16 * st + 4 * hf);
+                vsc[st][1] = *(const f32x4 *)(vs + 16 * st + 8 + 4 * hf);
+            }
+        }
+        if constexpr (C::K_SCALED && NEXT) {
+            const float *ks = (const float *)(kl + C::K_BYTES);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) ksc[kb][q4] = *(const f32x4 *)(ks + kb * 32 + q4 * 8 + hf * 4);
+        }
+        rescale(mx);
+        PA_FENCE();
+
+        // P = 2^(logit - m_run) for element e = 16 kb + i of tile kt; the fp16 B
+        // operand of PV step st takes elements 8 st .. 8 st + 7 (V scales folded in)
         float psum = 0.f;
+        f16x8 pb[4];
+        auto exp_el = [&](int e) {
+            const int kb = e >> 4, i = e & 15;
+            const float p = exp2_fast(fmaf(sc[kb][i], smfac, -m_run));
+            sc[kb][i] = p;
+            psum += p;
+            if ((e & 7) == 7) {
+                const int st = e >> 3, base = (st & 1) * 8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float x = sc[kb][base + j];
+                    pb[st][j] = (_Float16)(C::V_I8 ? x * vsc[st][j >> 2][j & 3] : x);
+                }
+            }
+        };
+
+        f32x16 sacc[2];
+        i32x16 sacci[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float pv = exp2_fast(fmaf(s[kb][i], smfac, -m_run));
-                s[kb][i] = pv;
-                psum += pv;
+                sacc[kb][i] = 0.f;
+                sacci[kb][i] = 0;
             }
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+                if (m + PFQ < NQ) ka[m + PFQ] = rdK(kr, m + PFQ);
+                else if (m + PFQ - NQ < VA) va[m + PFQ - NQ] = rdV(vr, m + PFQ - NQ);
+                copy_slot(m);
+                const int ks = m >> 1, kb = m & 1;
+                if constexpr (C::QK8)
+                    sacci[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bitcast<i32x4>(ka[m]), q8[ks], sacci[kb], 0, 0, 0);
+                else
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(ka[m]), qf[ks], sacc[kb], 0, 0, 0);
+#pragma unroll
+                for (int e = m * 32 / NQ; e < (m + 1) * 32 / NQ; ++e) exp_el(e);
+                PA_FENCE();
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) exp_el(e);
+            PA_FENCE();
+        }
         l_run += psum;
-    };
 
-    // ---- O^T += V^T P^T for one V stage: 4 steps of 16 keys x DB blocks of 32
-    // dims; A operands are read PF ahead of the MFMAs that use them
-    auto pv_tile = [&](int stage, const f32x16 (&s)[2]) {
-        const char *vl = vstage(stage);
-        const char *vr = vl + v_rd;
-        auto rd = [&](int i) -> f16x8 {
-            const int st = i / C::DB, db = i % C::DB;
-            return *(const f16x8 *)(vr + db * 32 * VT_ROW_BYTES + st * 32);
+        // tile kt+1's logit for element e: scale, mask, running maximum
+        float mxa = -INFINITY;
+        const int lim = my_pos - (kt + 1) * BN - hf * C::HSTEP;
+        auto post_el = [&](int e) {
+            const int kb = e >> 4, i = e & 15;
+            float v = C::QK8 ? (float)sacci[kb][i] : sacc[kb][i];
+            // per-key scale; the int8-QK arm also folds in sq * scale * log2e, so an
+            // all-zero query row (sq = 0) gives zero logits, never 0 * inf
+            if constexpr (C::K_SCALED) v *= ksc[kb][i >> 2][i & 3] * (C::QK8 ? lfac : 1.0f);
+            if constexpr (MASK)
+                if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) v = -INFINITY;
+            sn[kb][i] = v;
+            mxa = fmaxf(mxa, v);
         };
-        constexpr int NOPS = 4 * C::DB;
-        constexpr int PF = 3;
-        f16x8 a[PF + 1];
+
+        constexpr int VB = NEXT ? VA : PFV;             // V reads already issued
 #pragma unroll
-        for (int i = 0; i < PF; ++i) a[i] = rd(i);
-        f16x8 pb;
+        for (int n = VB; n < PFV; ++n) va[n] = rdV(vr, n);
 #pragma unroll
-        for (int i = 0; i < NOPS; ++i) {
-            const int st = i / C::DB, db = i % C::DB;
-            if (i + PF < NOPS) a[(i + PF) % (PF + 1)] = rd(i + PF);
-            if (db == 0) {
-                const int kb = st >> 1, base = (st & 1) * 8;
-                if constexpr (C::V_I8) {
-                    // fold each key's V scale into P: keys 16*st + 8*(j/4) + 4*hf + j%4
-                    const float *vs_lds = (const float *)(vl + C::V_BYTES);
-                    const f32x4 v0 = *(const f32x4 *)(vs_lds + 16 * st + 4 * hf);
-                    const f32x4 v1 = *(const f32x4 *)(vs_lds + 16 * st + 8 + 4 * hf);
+        for (int n = 0; n < NP; ++n) {
+            if (n + PFV < NP) va[n + PFV] = rdV(vr, n + PFV);
+            if constexpr (NEXT) copy_slot(NQ + n);
+            const int st = n / C::DB, db = n % C::DB;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pb[st], o[db], 0, 0, 0);
+            if constexpr (NEXT) {
+                if (n >= MB0) {
+                    constexpr int NS = NP - MB0;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pb[j] = (_Float16)(s[kb][base + j] * v0[j]);
-                        pb[4 + j] = (_Float16)(s[kb][base + 4 + j] * v1[j]);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) pb[j] = (_Float16)s[kb][base + j];
+                    for (int e = (n - MB0) * 32 / NS; e < (n - MB0 + 1) * 32 / NS; ++e) post_el(e);
                 }
             }
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i % (PF + 1)], pb, o[db], 0, 0, 0);
+            PA_FENCE();
         }
-    };
-
-    // ---- main loop: tile kt is in LDS stage kt & 1 while tile kt+1 streams in
-    f32x16 s[2];
-    dma_k(0, 0);
-    dma_v(0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < n_tiles) {
-            dma_k(kt + 1, cur ^ 1);
-            dma_v(kt + 1, cur ^ 1);
-        }
-        qk_tile(cur, s);
-        softmax_tile(s, kt);
-        pv_tile(cur, s);
+        if constexpr (NEXT) mx = max_halves(mxa) * smfac;
         __syncthreads();
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    // steps whose next tile is unmasked, two at a time (stages 0 then 1)
+    const int end1 = min(t_mask, n_tiles) - 1;
+    int kt = 0;
+    for (; kt + 1 < end1; kt += 2) {
+        step(kt, 0, sa, sb, yes{}, no{});
+        step(kt + 1, 1, sb, sa, yes{}, no{});
     }
+    if (kt < end1) {
+        step(kt, kt & 1, sa, sb, yes{}, no{});
+        ++kt;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+    }
+    // steps whose next tile is masked (the last one or two)
+    for (; kt + 1 < n_tiles; ++kt) {
+        step(kt, kt & 1, sa, sb, yes{}, yes{});
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+    }
+    step(kt, kt & 1, sa, sb, no{}, no{});
 
     // ---- epilogue: O / l, row of this lane's column
     const float l_tot = sum_halves(l_run);
@@ -549,10 +711,13 @@ static void launch_f(bool out_bf16, const AttnParams &p, dim3 grid, hipStream_t 
 template <int D, int KIND>
 static hipError_t launch_t(bool out_bf16, const AttnParams &p, dim3 grid, hipStream_t s) {
     if constexpr (KIND == KIND_BF16) {
-        // scalar-addressed K copies: blocks of >= 64 keys in whole multiples of
-        // 16, and a copy's per-lane offsets within 32 bits
-        const bool fast = p.block_size >= BN && p.block_size % 16 == 0 &&
-                          15 * p.stride_tok * 2 + 2 * D < ((int64_t)1 << 31);
+        // buffer-addressed K copies: blocks in whole multiples of 16 keys, the
+        // block-table row within the LDS cache, in-block offsets within 31 bits
+        using C = AttnCfg<D, KIND>;
+        const int64_t n_blk = ((int64_t)p.max_ctx + p.block_size - 1) / p.block_size;
+        const bool fast = p.block_size % 16 == 0 && n_blk <= C::BT_CAP &&
+                          (int64_t)(p.block_size - 1) * p.stride_tok * 2 +
+                                  (int64_t)(p.Hkv - 1) * p.stride_head * 2 + 2 * D < ((int64_t)1 << 31);
         if (fast)
             launch_f<D, KIND, true>(out_bf16, p, grid, s);
         else
