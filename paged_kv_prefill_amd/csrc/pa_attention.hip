@@ -72,7 +72,11 @@ constexpr float RESCALE_SLACK = 8.0f;   // lazy-rescale threshold, log2 units
 #define PA_PV_AHEAD 6
 #endif
 // LDS operand reads are issued this many MFMAs ahead of the MFMA that uses them
+#ifndef PA_PV_ORDER
+#define PA_PV_ORDER 1
+#endif
 constexpr int QK_AHEAD = PA_QK_AHEAD;
+constexpr int PV_ORDER = PA_PV_ORDER;
 constexpr int PV_AHEAD = PA_PV_AHEAD;
 #define PA_FENCE() __builtin_amdgcn_sched_barrier(0)
 static_assert(NTHR == ATTN_THREADS && NCOL == ATTN_COLS, "launch geometry");
@@ -137,6 +141,28 @@ __device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 }
 __device__ __forceinline__ void gdma16(const void *src, char *lds) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (LDS data ordering is explicit):
+// the compiler's fenced barrier would also wait for every copy in flight.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+// The same after this wave's direct-to-LDS copies, except the newest N, have
+// landed (s_waitcnt vmcnt(N); expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void barrier_lds_after_copies() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
 }
 
 // FAST (paged K only, chosen on the host): block_size a multiple of 16, so no
@@ -493,12 +519,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     f32x16 sa[2], sb[2];
     dma_k(0, 0);
     dma_v(0, 0);
-    if (n_tiles > 1) dma_k(1, 1);
+    dma_k(min(1, n_tiles - 1), 1);
     __syncthreads();
     qk_tile(0, sa);
     if (t_mask == 0) mask_tile(sa, 0);
     float mx = tile_max(sa);
     __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
+    dma_k(min(2, n_tiles - 1), 0);
 
     // ---- one pipelined step as a fixed sequence of slots.  Phase A: the QK
     // MFMAs of tile kt+1, each slot carrying one LDS operand read for a later
@@ -516,8 +543,12 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     auto rdK = [&](const char *kr, int m) -> u32x4 {
         return *(const u32x4 *)(kr + (m & 1) * C::KB_STEP + (m >> 1) * 32);
     };
+    // PV MFMA n -> (16-key step st, 32-dim block db): pairs of dim blocks take
+    // turns, so each accumulator is reused every other MFMA (as in QK)
+    auto pv_st = [](int n) { return PV_ORDER ? (n % 8) / 2 : n / C::DB; };
+    auto pv_db = [](int n) { return PV_ORDER ? 2 * (n / 8) + (n & 1) : n % C::DB; };
     auto rdV = [&](const char *vr, int n) -> f16x8 {
-        return *(const f16x8 *)(vr + (n % C::DB) * 32 * VT_ROW_BYTES + (n / C::DB) * 32);
+        return *(const f16x8 *)(vr + pv_db(n) * 32 * VT_ROW_BYTES + pv_st(n) * 32);
     };
 
     // HAS_NEXT: tile kt+1 exists; MASK_NEXT: it needs masking
@@ -528,18 +559,21 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         const char *kr = kl + k_rd;
         const char *vl = vstage(cur);
         const char *vr = vl + v_rd;
-        // copies of K(kt+2) and V(kt+1), one every other slot from the start of
-        // phase A (a tile index past the end re-copies the last tile into a stage
-        // nobody reads again, which keeps the slots branch-free)
-        const int tk = min(kt + 2, n_tiles - 1), tv = min(kt + 1, n_tiles - 1);
+        // copies: V(kt+1) during phase A (its stage held V(kt-1), done before the
+        // previous step's last barrier), K(kt+3) during phase B (its stage holds
+        // K(kt+1), done once every wave is past phase A), spread evenly over the
+        // slots.  A tile index past the end re-copies the last tile into a stage
+        // nobody reads again, which keeps the slots branch-free.
+        const int tk = min(kt + 3, n_tiles - 1), tv = min(kt + 1, n_tiles - 1);
         const KSrc ksrc = k_src(tk);
         const auto vsrc = v_src(tv);
-        auto copy_slot = [&](int slot) {
-            if (slot % 2 == 0) {
-                const int c = slot / 2;
-                if (c < NKC) k_copy(ksrc, tk, cur, c);
-                else if (c - NKC < NVC) v_copy(vsrc, cur ^ 1, c - NKC);
-            }
+        auto copy_a = [&](int slot) {
+#pragma unroll
+            for (int c = slot * NVC / NQ; c < (slot + 1) * NVC / NQ; ++c) v_copy(vsrc, cur ^ 1, c);
+        };
+        auto copy_b = [&](int slot) {
+#pragma unroll
+            for (int c = slot * NKC / NP; c < (slot + 1) * NKC / NP; ++c) k_copy(ksrc, tk, cur ^ 1, c);
         };
         u32x4 ka[NQ];
         f16x8 va[NP];
@@ -603,7 +637,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             for (int m = 0; m < NQ; ++m) {
                 if (m + PFQ < NQ) ka[m + PFQ] = rdK(kr, m + PFQ);
                 else if (m + PFQ - NQ < VA) va[m + PFQ - NQ] = rdV(vr, m + PFQ - NQ);
-                copy_slot(m);
+                copy_a(m);
                 const int ks = m >> 1, kb = m & 1;
                 if constexpr (C::QK8)
                     sacci[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bitcast<i32x4>(ka[m]), q8[ks], sacci[kb], 0, 0, 0);
@@ -619,6 +653,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             PA_FENCE();
         }
         l_run += psum;
+        // every wave is past phase A: K(kt+1)'s stage may take K(kt+3)
+        barrier_lds();
 
         // tile kt+1's logit for element e: scale, mask, running maximum
         float mxa = -INFINITY;
@@ -641,8 +677,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
             if (n + PFV < NP) va[n + PFV] = rdV(vr, n + PFV);
-            if constexpr (NEXT) copy_slot(NQ + n);
-            const int st = n / C::DB, db = n % C::DB;
+            if constexpr (NEXT) copy_b(n);
+            const int st = pv_st(n), db = pv_db(n);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pb[st], o[db], 0, 0, 0);
             if constexpr (NEXT) {
                 if (n >= MB0) {
@@ -654,7 +690,9 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             PA_FENCE();
         }
         if constexpr (NEXT) mx = max_halves(mxa) * smfac;
-        __syncthreads();
+        // V(kt+1) (issued in phase A) and K(kt+2) (issued in the previous step's
+        // phase B) have landed; the K(kt+3) copies may still be in flight
+        barrier_lds_after_copies<C::K_PER_WAVE>();
     };
     using yes = std::true_type;
     using no = std::false_type;
