@@ -1,20 +1,24 @@
 """Benchmark of chunked-prefill attention over a paged KV cache on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--arms all|none] [--no-cpu]
+                    [--calib-copy]
 
-One step is one launch of the bf16 prefill attention over the headline
-workload: a 2,048-token causal chunk at a 20,000-token context, head_dim 256,
-16 q / 4 KV heads, block 880, in a 2,600-block bf16 pool (the request placed at
-the top of the pool, blocks 2,577-2,599, so every offset needs 64 bits).  The
-timed region launches K steps back to back on torch's current stream; HIP
-events on that stream time each launch.  Inputs are seeded synthetic N(0,1)
-bf16 values, resident in HBM before timing starts.
+One step is one pa_prefill_bf16 call over the headline workload: a 2,048-token
+causal chunk at a 20,000-token context, head_dim 256, 16 q / 4 KV heads, block
+880, in a 2,600-block bf16 pool (the request placed at the top of the pool,
+blocks 2,577-2,599, so every offset needs 64 bits).  A call is the V image
+pass and the attention kernel.  The timed region launches K steps back to back
+on torch's current stream; HIP events on that stream time each launch.  Inputs
+are seeded synthetic N(0,1) bf16 values, resident in HBM before timing starts.
 
-Printed: one JSON line with the headline tokens/s, the roofline of the
-attention kernel (algorithmic FLOPs per launch / measured launch time against
-the bf16 dense MFMA peak), the CPU oracle's rate on a bounded sample, and the
-other arms (int8 KV exact-QK, int8-QK with its two K passes, fp8 KV through
-the dense bf16 scratch, the batched 8-request chunk) measured the same way.
+Printed: one JSON line with the headline tokens/s (whole calls), the roofline
+of the attention kernel alone (algorithmic FLOPs per launch / its measured
+launch time, against the bf16 dense MFMA peak; timed with the image pass
+skipped via PA_FLAG_IMAGES_READY), its HBM bytes per launch from the committed
+counter profile when that was taken on this build, the CPU oracle's rate on a
+bounded sample, and the other arms (int8 KV exact-QK, int8-QK with its two K
+passes, fp8 KV through the dense bf16 scratch, the batched 8-request chunk)
+measured per call.
 """
 from __future__ import annotations
 
@@ -159,7 +163,12 @@ def cpu_baseline(w, block_table, target_s: float = 12.0):
 
 
 # ------------------------------------------------------------------ arms
-def arm_bigpool_bf16(steps, warmup):
+def arm_bigpool_bf16(steps, warmup, calib=False):
+    """The headline: whole calls (V image pass + attention) for the value, and
+    the attention kernel alone (PA_FLAG_IMAGES_READY on the workspace the whole
+    calls filled) for the roofline.  With calib, also a plain gather of the
+    request's V rows (pa_gather_kv: bytes read = bytes written = known), the
+    reference the HBM byte counters are scaled by."""
     w = synth.config_bigpool_bf16()
     top = w.extra["top_block_table"]
     P = Pools(w, top)
@@ -167,9 +176,38 @@ def arm_bigpool_bf16(steps, warmup):
     out = P.out()
     ws = ops.workspace(p, ops.PA_ENTRY_PREFILL_BF16)
     fn = lambda: ops.pa_prefill_bf16(p, P.q, P.k, P.v, out, ws)
-    (ms,), wall = time_launches([fn], steps, warmup)
+    (ms_call,), wall = time_launches([fn], steps, warmup)
     assert torch.isfinite(out).all().item()
-    return w, top, ms, wall, attn_flops(w)
+    pa = P.paged()
+    pa.flags = ops.PA_FLAG_IMAGES_READY
+    fa = lambda: ops.pa_prefill_bf16(pa, P.q, P.k, P.v, out, ws)
+    (ms_attn,), _ = time_launches([fa], steps, 1)
+    assert torch.isfinite(out).all().item()
+    calib_bytes = None
+    if calib:
+        # the V pool: the attention-only launches just timed never read it, so its
+        # rows come from memory, not from L2
+        dense = torch.empty((int(w.ctx_lens[0]), w.num_kv_heads, w.head_dim), dtype=torch.bfloat16,
+                            device=DEV)
+        time_launches([lambda: ops.pa_gather_kv(p, P.v, P.cu_ctx, dense)], 3, 1)
+        calib_bytes = dense.numel() * 2
+    return w, top, ms_call, wall, ms_attn, attn_flops(w), calib_bytes
+
+
+def traffic_from_profile(build_id: str):
+    """HBM bytes per attention launch from the committed PMC summary, if it was
+    taken on this exact build; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "attn_bf16_bigpool_hbm_bytes.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("library") != build_id or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
 
 
 def arm_int8(steps, warmup):
@@ -268,6 +306,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--arms", default="all", choices=["all", "none"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain gather of known size (HBM counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -279,9 +319,10 @@ def main():
         sys.exit(1)
     ops.lib()   # fail loudly when the HIP library is not built
 
-    w, top, ms, wall, flops = arm_bigpool_bf16(args.steps, args.warmup)
+    w, top, ms_call, wall, ms, flops, calib_bytes = arm_bigpool_bf16(args.steps, args.warmup,
+                                                                    args.calib_copy)
     chunk = int(w.q_lens.sum())
-    achieved = flops / ms * 1e-9                     # TFLOP/s
+    achieved = flops / ms * 1e-9                     # TFLOP/s, attention kernel alone
     line = {
         "metric": METRIC,
         "value": chunk / (wall * 1e-3),
@@ -300,10 +341,14 @@ def main():
                                "2,600-block pool, request on blocks 2,577-2,599",
                    "global_batch": chunk, "seq_len": int(w.ctx_lens[0]), "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel_ms": ms, "flops_per_launch": flops},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profile(ops.build_id()),
+                     "kernel": "attn_kernel<256, bf16 KV>", "kernel_ms": ms,
+                     "call_ms": ms_call, "flops_per_launch": flops},
         "library": ops.build_id(),
     }
+    if calib_bytes is not None:
+        line["calib_copy_bytes"] = calib_bytes
     if args.arms == "all":
         arms = {}
         arms.update(arm_int8(args.steps, args.warmup))

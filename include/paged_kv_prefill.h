@@ -99,7 +99,15 @@ typedef struct pa_paged_args {
     int64_t stride_head;
     int64_t stride_sblock;        /* int8 per-token-head scale pool strides (elements)     */
     int64_t stride_stok;
+    int32_t flags;                /* PA_FLAG_* bits, 0 by default                          */
 } pa_paged_args;
+
+/* flags */
+/* The workspace already holds this call's tile images: an earlier attention
+ * call with the same entry point, arguments, pools and workspace built them,
+ * and neither V (nor, for pa_prefill_int8kv, K) has changed since.  The call
+ * then skips the image pass and launches the attention kernel alone. */
+#define PA_FLAG_IMAGES_READY 1
 
 /*
  * pa_prefill_bf16 -- chunked-prefill attention over a bf16 paged pool.

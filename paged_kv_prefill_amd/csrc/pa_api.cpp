@@ -38,6 +38,7 @@ int check_common(const pa_paged_args *a, int elem_bytes, bool needs_q) {
     if (a->max_ctx_len < 0 || a->max_q_len < 0 || (needs_q && a->max_q_len > a->max_ctx_len))
         return PA_ERR_SHAPE;
     if (a->causal != 0 && a->causal != 1) return PA_ERR_SHAPE;
+    if (a->flags & ~PA_FLAG_IMAGES_READY) return PA_ERR_SHAPE;
     if (!(a->softmax_scale > 0.0f) || a->softmax_scale == INFINITY) return PA_ERR_SHAPE;
     if (a->stride_block < 1 || a->stride_tok < 1 || a->stride_head < 1) return PA_ERR_SHAPE;
     // rows are read as 16-byte vectors: every row start must be 16-byte aligned
@@ -166,7 +167,8 @@ int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, c
     if ((rc = check_workspace(a, PA_ENTRY_PREFILL_BF16, workspace, workspace_bytes))) return rc;
     ImageParams ip = image_params(a, workspace, KIND_BF16);
     ip.src = v_pool;
-    if ((rc = launched(launch_images(ip, false, false, stream)))) return rc;
+    const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
+    if (build && (rc = launched(launch_images(ip, false, false, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.q = q;
     p.k = k_pool;
@@ -193,7 +195,8 @@ int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_poo
     ip.src_scales = v_scales;
     ip.src2 = k_pool;
     ip.src2_scales = k_scales;
-    if ((rc = launched(launch_images(ip, true, true, stream)))) return rc;
+    const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
+    if (build && (rc = launched(launch_images(ip, true, true, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.q = q;
     p.v_img = (const char *)ip.dst;
@@ -258,7 +261,8 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     ImageParams ip = image_params(a, workspace, kind);
     ip.src = v_pool;
     ip.src_scales = v_scales;
-    if ((rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8, false, stream)))) return rc;
+    const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
+    if (build && (rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8, false, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.cu_ctx = cu_ctx;
     p.q = q;

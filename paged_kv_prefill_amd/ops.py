@@ -21,6 +21,7 @@ PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_TOO_
 PA_ERR_WORKSPACE = -6
 PA_ENTRY_PREFILL_BF16, PA_ENTRY_PREFILL_INT8KV, PA_ENTRY_PREFILL_INT8QK = 1, 2, 3
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_INT8, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
+PA_FLAG_IMAGES_READY = 1
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_k_stats", "pa_k_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_gather_kv",
@@ -38,6 +39,7 @@ class PagedArgs(C.Structure):
         ("softmax_scale", C.c_float), ("causal", C.c_int32),
         ("stride_block", C.c_int64), ("stride_tok", C.c_int64), ("stride_head", C.c_int64),
         ("stride_sblock", C.c_int64), ("stride_stok", C.c_int64),
+        ("flags", C.c_int32),
     ]
 
 
@@ -122,6 +124,7 @@ class Paged:
     stride_block: Optional[int] = None
     stride_tok: Optional[int] = None
     stride_head: Optional[int] = None
+    flags: int = 0                     # PA_FLAG_* bits
 
     def args(self) -> PagedArgs:
         hkv, d, bs = self.num_kv_heads, self.head_dim, self.block_size
@@ -149,6 +152,7 @@ class Paged:
         a.stride_head = self.stride_head if self.stride_head is not None else d
         a.stride_sblock = bs * hkv
         a.stride_stok = hkv
+        a.flags = self.flags
         return a
 
 

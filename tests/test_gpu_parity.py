@@ -180,3 +180,42 @@ def test_fp8_every_code(orc):
         nan_got = (got & 0x7F80) == 0x7F80
         assert np.array_equal(nan_ref, nan_got)
         assert np.array_equal(got[~nan_ref], ref[~nan_ref])
+
+
+@pytest.mark.parametrize("arm", ["bf16", "int8kv", "int8qk"])
+def test_images_ready_flag(arm):
+    """PA_FLAG_IMAGES_READY on a workspace an identical call filled gives the
+    same bits; on a workspace of 0xFF bytes (NaN images) the output turns
+    non-finite, so the flag really skips the image pass."""
+    from paged_kv_prefill_amd import ops
+    g = gc()
+    w = synth.make_case(120, [37, 20], [300, 133], 64, 4, 2, 128,
+                        kv_format="bf16" if arm == "bf16" else "int8")
+    case = g.DevCase(w)
+    entry = {"bf16": ops.PA_ENTRY_PREFILL_BF16, "int8kv": ops.PA_ENTRY_PREFILL_INT8KV,
+             "int8qk": ops.PA_ENTRY_PREFILL_INT8QK}[arm]
+    ks, k8 = case.run_k_passes() if arm == "int8qk" else (None, None)
+
+    def call(flags, ws):
+        p = case.paged()
+        p.flags = flags
+        o = case.out()
+        if arm == "bf16":
+            ops.pa_prefill_bf16(p, case.q, case.k_pool, case.v_pool, o, ws=ws)
+        elif arm == "int8kv":
+            ops.pa_prefill_int8kv(p, case.q, case.k_pool, case.v_pool, case.k_scales,
+                                  case.v_scales, o, ws=ws)
+        else:
+            ops.pa_prefill_int8qk(p, case.q, k8, ks, case.cu_ctx, case.v_pool, case.v_scales, o,
+                                  ws=ws)
+        torch.cuda.synchronize()
+        return o
+
+    ws = ops.workspace(case.paged(), entry)
+    first = call(0, ws)
+    again = call(ops.PA_FLAG_IMAGES_READY, ws)
+    assert torch.isfinite(first).all().item()
+    assert torch.equal(first.view(torch.int32), again.view(torch.int32))
+    poisoned = torch.full_like(ws, 0xFF)
+    skipped = call(ops.PA_FLAG_IMAGES_READY, poisoned)
+    assert not torch.isfinite(skipped).all().item()

@@ -28,6 +28,15 @@ def test_header_declares_the_entry_points():
     assert set(names) == set(ops.ENTRY_POINTS)
 
 
+def test_struct_mirror_matches_header():
+    """ops.PagedArgs lists pa_paged_args' fields in the header's order and types."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct pa_paged_args \{(.*?)\} pa_paged_args;", text, re.S).group(1)
+    fields = re.findall(r"(const int32_t \*|int64_t|int32_t|float)\s*(\w+);", body)
+    ctype = {"const int32_t *": C.c_void_p, "int64_t": C.c_int64, "int32_t": C.c_int32, "float": C.c_float}
+    assert [(n, ctype[t]) for t, n in fields] == list(ops.PagedArgs._fields_)
+
+
 def test_library_exports_every_declared_symbol():
     lib = C.CDLL(ops.LIB_PATH)
     for n in declared_functions():
@@ -59,6 +68,7 @@ BAD = [
     (dict(causal=2), ops.PA_ERR_SHAPE),
     (dict(stride_tok=130), ops.PA_ERR_SHAPE),
     (dict(max_ctx_len=2 ** 30, max_q_len=8), ops.PA_ERR_TOO_LARGE),
+    (dict(flags=2), ops.PA_ERR_SHAPE),
 ]
 
 
@@ -110,18 +120,31 @@ def test_workspace_size_formula():
     assert L.pa_workspace_bytes(C.byref(_args(num_q_heads=3)), ops.PA_ENTRY_PREFILL_BF16) == 0
 
 
+def golden(name):
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", name)):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = (x.strip() for x in line.split("=", 1))
+            vals[k] = int(v)
+    return vals
+
+
 def test_pool_geometry_matches_pages():
-    """Block stride 880 * 4 * 256 = 901,120 elements; the int32 product
-    overflows from block 2,384 on, so ids above 2,383 are the unsafe ones; the
-    top placement of the 2,600-block pool clears that by 217 blocks (HyperQwen
-    PR #91, blocking review)."""
+    """The big-pool workload has the geometry the pages print
+    (tests/golden/pages_geometry.txt, each number with its passage): block
+    stride 901,120 elements, int32 products safe up to block 2,383, the top
+    placement clearing that by 217 blocks."""
+    g = golden("pages_geometry.txt")
     w = synth.config_bigpool_bf16()
-    assert w.stride_block == 901_120
-    assert 2383 * w.stride_block < 2 ** 31 <= 2384 * w.stride_block
+    assert w.stride_block == g["block_stride_elements"] == 880 * 4 * 256
+    safe = g["last_safe_block_id"]
+    assert safe * w.stride_block < 2 ** 31 <= (safe + 1) * w.stride_block
     top = w.extra["top_block_table"]
-    assert top.shape == (1, 23) and int(top.min()) == 2577 and int(top.max()) == 2599
-    assert w.num_blocks - 2383 == 217
-    assert w.block_table.tolist() == [list(range(23))]
+    assert int(top.min()) == g["top_first_block"] and int(top.max()) == g["top_last_block"]
+    assert w.num_blocks == g["pool_blocks"] and w.num_blocks - safe == g["margin_blocks"]
+    assert w.block_table.tolist() == [list(range(g["bottom_last_block"] + 1))]
+    assert int(w.ctx_lens[0]) == g["context_tokens"] and int(w.q_lens[0]) == g["chunk_tokens"]
     assert int(w.ctx_lens[0]) - 22 * 880 == 640          # valid slots in the last block
 
 
