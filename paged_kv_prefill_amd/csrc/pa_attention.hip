@@ -296,16 +296,26 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         __amdgpu_buffer_rsrc_t rs;
         uint32_t soff;
     };
-    auto k_src = [&](int kt) -> KSrc {
-        const int kbase = kt * BN;
+    // the block id behind a wave's copies of tile kt: an LDS read issued early
+    // (k_src_id) and consumed later (k_src), so its latency hides behind MFMAs
+    auto k_src_key = [&](int kt) { return min(kt * BN + wave_u * 16, (n_keys - 1) & ~15); };
+    auto k_src_id = [&](int kt) -> int {
+        if constexpr (C::K_PAGED && FAST) {
+            FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
+            return bt_lds[(int)fdiv((uint32_t)k_src_key(kt), fd)];
+        } else {
+            return 0;
+        }
+    };
+    auto k_src = [&](int kt, int raw_id) -> KSrc {
         if constexpr (C::K_PAGED && FAST) {
             // a wave's copies cover 16 consecutive keys, so one cache block; a
             // wave whose keys are all past the context re-reads the last 16
             // inside it
             FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
-            const int kw = min(kbase + wave_u * 16, (n_keys - 1) & ~15);
+            const int kw = k_src_key(kt);
             const int b = (int)fdiv((uint32_t)kw, fd);
-            int id = __builtin_amdgcn_readfirstlane(bt_lds[b]);
+            int id = __builtin_amdgcn_readfirstlane(raw_id);
             id = (uint32_t)id < nb32 ? id : 0;   // an id outside the pool reads block 0 (caller error)
             return KSrc{rsrc_at((const char *)P.k + (int64_t)id * sbb + ghb),
                         (uint32_t)((kw - b * P.block_size) * stb)};
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     };
     constexpr int NKC = C::K_PER_WAVE + (C::K_SCALED ? 1 : 0);   // K copy instructions per wave
     auto dma_k = [&](int kt, int stage) {
-        const KSrc src = k_src(kt);
+        const KSrc src = k_src(kt, k_src_id(kt));
 #pragma unroll
         for (int i = 0; i < NKC; ++i) k_copy(src, kt, stage, i);
     };
@@ -552,7 +562,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     };
 
     // HAS_NEXT: tile kt+1 exists; MASK_NEXT: it needs masking
-    auto step = [&](int kt, int cur, f32x16 (&sc)[2], f32x16 (&sn)[2], auto has_next, auto mask_next) {
+    // kin: the first PFQ K operands of tile kt+1, read by the previous step;
+    // kout: the same for tile kt+2, read here in phase B
+    auto step = [&](int kt, int cur, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&kin)[PFQ],
+                    u32x4 (&kout)[PFQ], auto has_next, auto mask_next) {
         constexpr bool NEXT = decltype(has_next)::value;
         constexpr bool MASK = decltype(mask_next)::value;
         const char *kl = kstage(cur ^ 1);
@@ -565,7 +578,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         // slots.  A tile index past the end re-copies the last tile into a stage
         // nobody reads again, which keeps the slots branch-free.
         const int tk = min(kt + 3, n_tiles - 1), tv = min(kt + 1, n_tiles - 1);
-        const KSrc ksrc = k_src(tk);
+        const int kid_raw = k_src_id(tk);
+        KSrc ksrc;
         const auto vsrc = v_src(tv);
         auto copy_a = [&](int slot) {
 #pragma unroll
@@ -581,7 +595,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         f32x4 ksc[2][4];
         if constexpr (NEXT) {
 #pragma unroll
-            for (int m = 0; m < PFQ; ++m) ka[m] = rdK(kr, m);
+            for (int m = 0; m < PFQ; ++m) ka[m] = kin[m];
         } else {
 #pragma unroll
             for (int n = 0; n < PFV; ++n) va[n] = rdV(vr, n);
@@ -653,8 +667,12 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             PA_FENCE();
         }
         l_run += psum;
-        // every wave is past phase A: K(kt+1)'s stage may take K(kt+3)
-        barrier_lds();
+        // every wave is past phase A, so K(kt+1)'s stage may take K(kt+3), and
+        // every wave's K(kt+2) copies (issued before this step's V copies) have
+        // landed, so phase B may read ahead into tile kt+2
+        barrier_lds_after_copies<C::VCOPIES / NWAVE>();
+        if constexpr (NEXT) ksrc = k_src(tk, kid_raw);
+        const char *kr2 = kstage(cur) + k_rd;
 
         // tile kt+1's logit for element e: scale, mask, running maximum
         float mxa = -INFINITY;
@@ -677,7 +695,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
             if (n + PFV < NP) va[n + PFV] = rdV(vr, n + PFV);
-            if constexpr (NEXT) copy_b(n);
+            if constexpr (NEXT) {
+                copy_b(n);
+                if (n >= NP - PFQ) kout[n - (NP - PFQ)] = rdK(kr2, n - (NP - PFQ));
+            }
             const int st = pv_st(n), db = pv_db(n);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pb[st], o[db], 0, 0, 0);
             if constexpr (NEXT) {
@@ -696,26 +717,36 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     };
     using yes = std::true_type;
     using no = std::false_type;
+    u32x4 ka0[PFQ], ka1[PFQ];
+#pragma unroll
+    for (int m = 0; m < PFQ; ++m) ka0[m] = rdK(kstage(1) + k_rd, m);   // K(1), landed
     // steps whose next tile is unmasked, two at a time (stages 0 then 1)
     const int end1 = min(t_mask, n_tiles) - 1;
     int kt = 0;
     for (; kt + 1 < end1; kt += 2) {
-        step(kt, 0, sa, sb, yes{}, no{});
-        step(kt + 1, 1, sb, sa, yes{}, no{});
+        step(kt, 0, sa, sb, ka0, ka1, yes{}, no{});
+        step(kt + 1, 1, sb, sa, ka1, ka0, yes{}, no{});
     }
-    if (kt < end1) {
-        step(kt, kt & 1, sa, sb, yes{}, no{});
-        ++kt;
+    auto roll = [&]() {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+#pragma unroll
+        for (int m = 0; m < PFQ; ++m) ka0[m] = ka1[m];
+    };
+    if (kt < end1) {
+        step(kt, kt & 1, sa, sb, ka0, ka1, yes{}, no{});
+        ++kt;
+        roll();
     }
     // steps whose next tile is masked (the last one or two)
     for (; kt + 1 < n_tiles; ++kt) {
-        step(kt, kt & 1, sa, sb, yes{}, yes{});
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+        step(kt, kt & 1, sa, sb, ka0, ka1, yes{}, yes{});
+        roll();
     }
-    step(kt, kt & 1, sa, sb, no{}, no{});
+    step(kt, kt & 1, sa, sb, ka0, ka1, no{}, no{});
+    // copies still in flight (the last steps re-copy into stages nobody reads)
+    // land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
 
     // ---- epilogue: O / l, row of this lane's column
     const float l_tot = sum_halves(l_run);
