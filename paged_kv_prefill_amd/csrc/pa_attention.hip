@@ -72,11 +72,11 @@ constexpr float RESCALE_SLACK = 8.0f;   // lazy-rescale threshold, log2 units
 #define PA_PV_AHEAD 6
 #endif
 // LDS operand reads are issued this many MFMAs ahead of the MFMA that uses them
-#ifndef PA_PV_ORDER
-#define PA_PV_ORDER 1
+#ifndef PA_PV_IN_A
+#define PA_PV_IN_A 0
 #endif
 constexpr int QK_AHEAD = PA_QK_AHEAD;
-constexpr int PV_ORDER = PA_PV_ORDER;
+constexpr int PV_IN_A = PA_PV_IN_A;      // PV MFMAs in phase A per 24 of its PV-capable slots
 constexpr int PV_AHEAD = PA_PV_AHEAD;
 #define PA_FENCE() __builtin_amdgcn_sched_barrier(0)
 static_assert(NTHR == ATTN_THREADS && NCOL == ATTN_COLS, "launch geometry");
@@ -403,8 +403,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     const int k_rd = K_COPY_STRIDE * (lc % C::KCOPIES) + (lc / C::KCOPIES) * C::K_ROW_BYTES + hf * 16;
     const int v_rd = lc * VT_ROW_BYTES + hf * 16;
 
-    // ---- S^T = K Q^T for the 2 blocks of 32 keys of a K stage (logits in
-    // log2 units for the int8-QK arm, raw otherwise); A operands are read two
+    // ---- S^T = K Q^T for the 2 blocks of 32 keys of a K stage (raw logits, the
+    // int8-QK arm's times the key scale); A operands are read two
     // k-steps ahead of the MFMAs that use them
     auto qk_tile = [&](int stage, f32x16 (&s)[2]) {
         const char *kl = kstage(stage);
@@ -455,18 +455,15 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[kb][i] = (float)si[kb][i];
         }
-        if constexpr (C::K_SCALED) {
-            // per-key scale; the int8-QK arm also folds in sq * scale * log2e, so an
-            // all-zero query row (sq = 0) gives zero logits, never 0 * inf
+        if constexpr (C::K_SCALED) {   // per-key scale
             const float *ks_lds = (const float *)(kl + C::K_BYTES);
-            const float f = C::QK8 ? lfac : 1.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const f32x4 kk = *(const f32x4 *)(ks_lds + kb * 32 + q4 * 8 + hf * 4);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) s[kb][q4 * 4 + i] *= kk[i] * f;
+                    for (int i = 0; i < 4; ++i) s[kb][q4 * 4 + i] *= kk[i];
                 }
         }
     };
@@ -477,7 +474,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    const float smfac = C::QK8 ? 1.0f : lfac;   // logit -> log2 units in the softmax
+    // logit -> log2 units, applied by the softmax's own multiply-add: the int8-QK
+    // logits stay int dot * key scale until then, and an all-zero query row (sq
+    // = 0, so lfac = 0) gives zero logits, never 0 * inf
+    const float smfac = lfac;
     float m_run = -INFINITY;   // running (lazy) max of the log2-domain logits
     float l_run = 0.f;         // this half-wave's share of the running sum
 
@@ -548,17 +548,18 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     constexpr int NP = 4 * C::DB;                      // PV MFMAs per tile
     constexpr int PFQ = QK_AHEAD < NQ ? QK_AHEAD : NQ;
     constexpr int PFV = PV_AHEAD < NP ? PV_AHEAD : NP;
-    constexpr int VA = PFQ < PFV ? PFQ : PFV;          // V reads issued in phase A
-    constexpr int MB0 = NP > 4 ? 2 : 0;                // first phase-B slot touching S(kt+1)
+    // phase A's slot LAG is the first whose exponentials complete P's first key
+    // step: from there on a phase-A slot also carries a PV MFMA
+    constexpr int LAG = NQ / 4;
+    static_assert(C::DB >= LAG, "P key step st is ready by PV MFMA st * DB");
+    // PV MFMAs spread over phase A's slots LAG.. (the rest go to phase B, where
+    // they carry tile kt+1's post-processing)
+    constexpr int NPA = (PV_IN_A * (NQ - LAG)) / 24 < NP ? (PV_IN_A * (NQ - LAG)) / 24 : NP;
     auto rdK = [&](const char *kr, int m) -> u32x4 {
         return *(const u32x4 *)(kr + (m & 1) * C::KB_STEP + (m >> 1) * 32);
     };
-    // PV MFMA n -> (16-key step st, 32-dim block db): pairs of dim blocks take
-    // turns, so each accumulator is reused every other MFMA (as in QK)
-    auto pv_st = [](int n) { return PV_ORDER ? (n % 8) / 2 : n / C::DB; };
-    auto pv_db = [](int n) { return PV_ORDER ? 2 * (n / 8) + (n & 1) : n % C::DB; };
-    auto rdV = [&](const char *vr, int n) -> f16x8 {
-        return *(const f16x8 *)(vr + pv_db(n) * 32 * VT_ROW_BYTES + pv_st(n) * 32);
+    auto rdV = [&](const char *vr, int n) -> f16x8 {   // V^T operand of PV MFMA n
+        return *(const f16x8 *)(vr + (n % C::DB) * 32 * VT_ROW_BYTES + (n / C::DB) * 32);
     };
 
     // HAS_NEXT: tile kt+1 exists; MASK_NEXT: it needs masking
@@ -568,6 +569,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                     u32x4 (&kout)[PFQ], auto has_next, auto mask_next) {
         constexpr bool NEXT = decltype(has_next)::value;
         constexpr bool MASK = decltype(mask_next)::value;
+        constexpr int N0 = NEXT ? NPA : 0;             // PV MFMAs issued in phase A
+        constexpr int NB = NP - N0;                    // phase-B slots
         const char *kl = kstage(cur ^ 1);
         const char *kr = kl + k_rd;
         const char *vl = vstage(cur);
@@ -587,18 +590,17 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         };
         auto copy_b = [&](int slot) {
 #pragma unroll
-            for (int c = slot * NKC / NP; c < (slot + 1) * NKC / NP; ++c) k_copy(ksrc, tk, cur ^ 1, c);
+            for (int c = slot * NKC / NB; c < (slot + 1) * NKC / NB; ++c) k_copy(ksrc, tk, cur ^ 1, c);
         };
         u32x4 ka[NQ];
         f16x8 va[NP];
         f32x4 vsc[4][2];
         f32x4 ksc[2][4];
+#pragma unroll
+        for (int n = 0; n < PFV; ++n) va[n] = rdV(vr, n);
         if constexpr (NEXT) {
 #pragma unroll
             for (int m = 0; m < PFQ; ++m) ka[m] = kin[m];
-        } else {
-#pragma unroll
-            for (int n = 0; n < PFV; ++n) va[n] = rdV(vr, n);
         }
         if constexpr (C::V_I8) {
             const float *vs = (const float *)(vl + C::V_BYTES);
@@ -636,6 +638,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 }
             }
         };
+        // PV MFMA n: O^T[dims of block n % DB] += V^T P^T over key step n / DB,
+        // its V^T operand read PFV MFMAs ahead
+        auto pv = [&](int n) {
+            if (n + PFV < NP) va[n + PFV] = rdV(vr, n + PFV);
+            const int st = n / C::DB, db = n % C::DB;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pb[st], o[db], 0, 0, 0);
+        };
 
         f32x16 sacc[2];
         i32x16 sacci[2];
@@ -647,10 +656,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 sacci[kb][i] = 0;
             }
         if constexpr (NEXT) {
+            // phase A: QK MFMA m of tile kt+1, tile kt's exponentials, and from
+            // slot LAG on (once P's first key step is ready) PV MFMA m - LAG of tile kt
 #pragma unroll
             for (int m = 0; m < NQ; ++m) {
                 if (m + PFQ < NQ) ka[m + PFQ] = rdK(kr, m + PFQ);
-                else if (m + PFQ - NQ < VA) va[m + PFQ - NQ] = rdV(vr, m + PFQ - NQ);
                 copy_a(m);
                 const int ks = m >> 1, kb = m & 1;
                 if constexpr (C::QK8)
@@ -659,6 +669,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(ka[m]), qf[ks], sacc[kb], 0, 0, 0);
 #pragma unroll
                 for (int e = m * 32 / NQ; e < (m + 1) * 32 / NQ; ++e) exp_el(e);
+                if (m >= LAG) {
+#pragma unroll
+                    for (int n = (m - LAG) * NPA / (NQ - LAG); n < (m - LAG + 1) * NPA / (NQ - LAG); ++n) pv(n);
+                }
                 PA_FENCE();
             }
         } else {
@@ -680,33 +694,26 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         auto post_el = [&](int e) {
             const int kb = e >> 4, i = e & 15;
             float v = C::QK8 ? (float)sacci[kb][i] : sacc[kb][i];
-            // per-key scale; the int8-QK arm also folds in sq * scale * log2e, so an
-            // all-zero query row (sq = 0) gives zero logits, never 0 * inf
-            if constexpr (C::K_SCALED) v *= ksc[kb][i >> 2][i & 3] * (C::QK8 ? lfac : 1.0f);
+            if constexpr (C::K_SCALED) v *= ksc[kb][i >> 2][i & 3];   // per-key scale
             if constexpr (MASK)
                 if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) v = -INFINITY;
             sn[kb][i] = v;
             mxa = fmaxf(mxa, v);
         };
 
-        constexpr int VB = NEXT ? VA : PFV;             // V reads already issued
+        // phase B: the remaining PV MFMAs with the K(kt+3) copies, the first
+        // operand reads of tile kt+2 and tile kt+1's post-processing
 #pragma unroll
-        for (int n = VB; n < PFV; ++n) va[n] = rdV(vr, n);
-#pragma unroll
-        for (int n = 0; n < NP; ++n) {
-            if (n + PFV < NP) va[n + PFV] = rdV(vr, n + PFV);
+        for (int j = 0; j < NB; ++j) {
             if constexpr (NEXT) {
-                copy_b(n);
-                if (n >= NP - PFQ) kout[n - (NP - PFQ)] = rdK(kr2, n - (NP - PFQ));
+                copy_b(j);
+#pragma unroll
+                for (int k = j * PFQ / NB; k < (j + 1) * PFQ / NB; ++k) kout[k] = rdK(kr2, k);
             }
-            const int st = pv_st(n), db = pv_db(n);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pb[st], o[db], 0, 0, 0);
+            pv(N0 + j);
             if constexpr (NEXT) {
-                if (n >= MB0) {
-                    constexpr int NS = NP - MB0;
 #pragma unroll
-                    for (int e = (n - MB0) * 32 / NS; e < (n - MB0 + 1) * 32 / NS; ++e) post_el(e);
-                }
+                for (int e = j * 32 / NB; e < (j + 1) * 32 / NB; ++e) post_el(e);
             }
             PA_FENCE();
         }
