@@ -28,29 +28,34 @@
 // leaves registers.
 //
 // Data movement.  Tiles are double-buffered in LDS and move with gfx950's
-// direct global-to-LDS copies (global_load_lds_dwordx4, 1 KB per wave
+// direct global-to-LDS copies (buffer_load_dwordx4 ... lds, 1 KB per wave
 // instruction, no registers).  A K copy takes the rows of 1024 / R consecutive
 // keys (R = bytes per key row); with block_size a multiple of 16 those keys
-// sit in one cache block, so the copy's address is a wave-uniform scalar (block
-// id read through the scalar cache, widened to 64 bits) plus a
-// per-lane constant, and the loop spends no vector instructions on it.  V comes
-// from the per-tile V^T images that pa_images.hip builds once per call.  The
-// tile layouts (pa_layout.h) pad rows instead of swizzling them, so every
-// operand read of a lane is one base register plus an immediate offset and no
-// LDS read conflicts.  The copies of tile t+1 are issued before the MFMAs of
-// tile t; one barrier per tile.  The running maximum is updated lazily: O and
-// the row sum are rescaled only when some column's maximum grows by more than
-// 2^8 (log2 units).
+// sit in one cache block, so the copy's source is a wave-uniform buffer
+// descriptor (the block id comes from the request's block-table row, copied
+// to LDS once and widened to 64 bits) plus a per-lane constant, and the loop
+// spends no vector instructions on addresses.  V comes from the per-tile V^T
+// images that pa_images.hip builds once per call.  The tile layouts
+// (pa_layout.h) pad rows instead of swizzling them, so every operand read of
+// a lane is one base register plus an immediate offset and no LDS read
+// conflicts.
+//
+// Pipeline.  Step t runs, as a fixed program of slots separated by scheduling
+// fences, the QK MFMAs of tile t+1 beside tile t's exponentials (phase A) and
+// the PV MFMAs of tile t beside tile t+1's scaling, masking and maximum
+// (phase B), with the direct copies of V(t+1) and K(t+3) spread between the
+// MFMAs and one barrier after each phase.  The running maximum is updated
+// lazily: O and the row sum are rescaled only when some column's maximum grows
+// by more than 8 (log2 units), so P stays within [0, 2^8].
 //
 // The int8-QK arm replaces the QK MFMA with v_mfma_i32_32x32x32_i8 on the
 // int8 K written by the K-quant pass and on Q quantised per (token, head) in
-// the prologue.  The int8-KV arms keep the codes: a per-token-head scale is
-// constant along the head dimension, so <q, code * s> = s * <q, code> and
-// sum_j p_j (code_j * s_j) = sum_j (p_j * s_j) code_j.  Codes (|c| <= 127) are
-// exact in bf16 and fp16, so the K tile holds codes for the bf16 QK MFMA and
-// the logits are scaled per key afterwards, and the V^T tile holds codes for
-// the fp16 PV MFMA with each key's V scale folded into P.  No dequantised
-// value is ever rounded.
+// the prologue.  The exact-QK int8-KV arm keeps the K codes: a per-token-head
+// scale is constant along the head dimension, so <q, code * s> = s * <q, code>;
+// codes (|c| <= 127) are exact in bf16, so the K tile holds codes for the bf16
+// QK MFMA and the logits are scaled per key afterwards.  Both int8 arms take V
+// dequantised by the image pass (code * scale rounded once to fp16), so their
+// PV is the bf16 arm's.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -84,7 +89,6 @@ static_assert(NTHR == ATTN_THREADS && NCOL == ATTN_COLS, "launch geometry");
 template <int D, int KIND>
 struct AttnCfg {
     static constexpr bool QK8 = (KIND == KIND_QK8_VBF16 || KIND == KIND_QK8_VI8);
-    static constexpr bool V_I8 = (KIND == KIND_I8KV || KIND == KIND_QK8_VI8);  // V codes + scales
     static constexpr bool K_I8 = (KIND == KIND_I8KV);      // K tile images of int8 codes + scales
     static constexpr bool K_PAGED = (KIND == KIND_BF16);   // K straight from the bf16 pool
     static constexpr bool K_SCALED = K_I8 || QK8;          // logits need a per-key scale
@@ -96,7 +100,9 @@ struct AttnCfg {
     static constexpr int V_BYTES = vt_tile_bytes(D);
     static constexpr int VCOPIES = V_BYTES / 1024;
     static constexpr int KSTAGE = K_BYTES + (K_SCALED ? BN * 4 : 0);
-    static constexpr int VSTAGE = V_BYTES + (V_I8 ? BN * 4 : 0);
+    // int8 V reaches the kernel dequantised (code x scale, fp16) in its image,
+    // like bf16 V, so a V stage is the V^T tile alone
+    static constexpr int VSTAGE = V_BYTES;
     static constexpr int BT_OFF = 2 * KSTAGE + 2 * VSTAGE;
     // block-table entries cached in LDS by the FAST paged path
     static constexpr int BT_CAP = K_PAGED ? ((LDS_MAX - BT_OFF) / 4 < 4096 ? (LDS_MAX - BT_OFF) / 4 : 4096) : 0;
@@ -383,16 +389,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     auto v_src = [&](int kt) { return rsrc_at(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D)); };
     auto v_copy = [&](__amdgpu_buffer_rsrc_t img, int stage, int i) {
         char *vl = vstage(stage);
-        if (i == C::V_PER_WAVE) {   // per-key scales
-            if constexpr (C::V_I8) {
-                if (wave_u == NWAVE - 1) bdma4(img, lane * 4, C::V_BYTES, vl + C::V_BYTES);
-            }
-            return;
-        }
         const int q = i * NWAVE + wave_u;
         if (C::VCOPIES % NWAVE == 0 || q < C::VCOPIES) bdma16(img, lane * 16, q * 1024, vl + q * 1024);
     };
-    constexpr int NVC = C::V_PER_WAVE + (C::V_I8 ? 1 : 0);       // V copy instructions per wave
+    constexpr int NVC = C::V_PER_WAVE;                           // V copy instructions per wave
     auto dma_v = [&](int kt, int stage) {
         const auto img = v_src(kt);
 #pragma unroll
@@ -594,21 +594,12 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         };
         u32x4 ka[NQ];
         f16x8 va[NP];
-        f32x4 vsc[4][2];
         f32x4 ksc[2][4];
 #pragma unroll
         for (int n = 0; n < PFV; ++n) va[n] = rdV(vr, n);
         if constexpr (NEXT) {
 #pragma unroll
             for (int m = 0; m < PFQ; ++m) ka[m] = kin[m];
-        }
-        if constexpr (C::V_I8) {
-            const float *vs = (const float *)(vl + C::V_BYTES);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                vsc[st][0] = *(const f32x4 *)(vs + 16 * st + 4 * hf);
-                vsc[st][1] = *(const f32x4 *)(vs + 16 * st + 8 + 4 * hf);
-            }
         }
         if constexpr (C::K_SCALED && NEXT) {
             const float *ks = (const float *)(kl + C::K_BYTES);
@@ -621,7 +612,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         PA_FENCE();
 
         // P = 2^(logit - m_run) for element e = 16 kb + i of tile kt; the fp16 B
-        // operand of PV step st takes elements 8 st .. 8 st + 7 (V scales folded in)
+        // operand of PV step st takes elements 8 st .. 8 st + 7
         float psum = 0.f;
         f16x8 pb[4];
         auto exp_el = [&](int e) {
@@ -632,10 +623,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             if ((e & 7) == 7) {
                 const int st = e >> 3, base = (st & 1) * 8;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float x = sc[kb][base + j];
-                    pb[st][j] = (_Float16)(C::V_I8 ? x * vsc[st][j >> 2][j & 3] : x);
-                }
+                for (int j = 0; j < 8; ++j) pb[st][j] = (_Float16)sc[kb][base + j];
             }
         };
         // PV MFMA n: O^T[dims of block n % DB] += V^T P^T over key step n / DB,

@@ -14,9 +14,11 @@
 //
 // The pass reads the paged pool through the block table with 64-bit offsets,
 // stages each tile through LDS (V^T is a transpose) and writes the image with
-// coalesced 16-byte stores.  int8 codes are kept as codes (exact in bf16 and
-// fp16) and their per-token-head scales go to the image's scale vector.
-// Keys at or past the context length are zero (scale 0).
+// coalesced 16-byte stores.  int8 V codes are dequantised here (code x its
+// per-token-head scale, rounded once to fp16), so the attention kernel's PV
+// takes them like bf16 V; the scales also go to the image's scale vector.
+// K codes (the exact-QK arm's K image) are kept as codes, exact in bf16, with
+// their scales.  Keys at or past the context length are zero (scale 0).
 #include "pa_device.h"
 #include "pa_kernels.h"
 #include "pa_layout.h"
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
             for (int e = 0; e < 16; ++e) {
                 float x[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = (float)(int8_t)((w[j][e >> 2] >> ((e & 3) * 8)) & 0xff);
+                for (int j = 0; j < 4; ++j) x[j] = (float)(int8_t)((w[j][e >> 2] >> ((e & 3) * 8)) & 0xff) * s[j];
                 *(u32x2 *)(img + vt_off(dc * 16 + e, slot)) =
                     u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
             }
