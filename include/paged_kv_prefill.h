@@ -33,9 +33,12 @@
  *     pa_workspace_bytes(args, entry) bytes (16-byte aligned).  Each call first
  *     lays the request's V (and, for pa_prefill_int8kv, K) out once as per-tile
  *     images in the kernel's LDS layout (64 keys per tile: a transposed fp16 V
- *     tile, or a bf16 code K tile, plus 64 fp32 per-key scales), then runs the
- *     attention, both on `stream`.  Calls that overlap on the same workspace
- *     race.
+ *     tile, int8 V dequantised, or a bf16 code K tile, plus 64 fp32 per-key
+ *     scales) and writes the attention's work schedule (which workgroup takes
+ *     which 128-column tile of which request and KV head, balancing the work
+ *     of requests of different lengths over the GPU's eight XCDs), then runs
+ *     the attention, all on `stream`.  Calls that overlap on the same
+ *     workspace race.
  *   - Return value: PA_OK (0), or a negative PA_ERR_* code.  On an argument
  *     error nothing is enqueued.  PA_ERR_LAUNCH means the launch itself failed
  *     (hipGetLastError after the launch).  No C++ exception crosses the ABI.
@@ -103,10 +106,11 @@ typedef struct pa_paged_args {
 } pa_paged_args;
 
 /* flags */
-/* The workspace already holds this call's tile images: an earlier attention
- * call with the same entry point, arguments, pools and workspace built them,
- * and neither V (nor, for pa_prefill_int8kv, K) has changed since.  The call
- * then skips the image pass and launches the attention kernel alone. */
+/* The workspace already holds this call's tile images and work schedule: an
+ * earlier attention call with the same entry point, arguments, pools and
+ * workspace built them, and neither V (nor, for pa_prefill_int8kv, K) nor the
+ * lengths have changed since.  The call then skips the image and schedule
+ * passes and launches the attention kernel alone. */
 #define PA_FLAG_IMAGES_READY 1
 
 /*
@@ -181,7 +185,10 @@ int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8
  * these arguments: n = num_reqs * ceil(max_ctx_len / 64) * num_kv_heads V tile
  * images of 144 * head_dim + 256 bytes (fp16 rows of 64 keys padded to 72,
  * plus scales), and for PA_ENTRY_PREFILL_INT8KV n more K tile images of
- * 128 * head_dim + 256 bytes.
+ * 128 * head_dim + 256 bytes; then, from the next multiple of 256 bytes, the
+ * work schedule: 4 bytes per attention workgroup, num_reqs * num_kv_heads *
+ * ceil(max_q_len * (num_q_heads / num_kv_heads) / 128) rounded up to a
+ * multiple of 8.
  * Returns 0 for invalid arguments or an unknown entry.
  */
 size_t pa_workspace_bytes(const pa_paged_args *args, int32_t entry);

@@ -113,12 +113,19 @@ int64_t image_count(const pa_paged_args *a) {
     return (int64_t)a->num_reqs * tiles_per_request(a->max_ctx_len) * a->num_kv_heads;
 }
 
-// bytes of workspace an attention entry point needs: V^T tile images, plus K
-// tile images for the int8-KV exact arm
-int64_t workspace_need(const pa_paged_args *a, int32_t entry) {
+// workspace of an attention entry point: V^T tile images, K tile images for
+// the int8-KV exact arm, then (256-byte aligned) the work schedule, one int32
+// per attention workgroup
+int64_t sched_offset(const pa_paged_args *a, int32_t entry) {
     const int64_t n = image_count(a);
-    return n * v_image_bytes(a->head_dim) +
-           (entry == PA_ENTRY_PREFILL_INT8KV ? n * k_image_bytes(a->head_dim) : 0);
+    const int64_t img = n * v_image_bytes(a->head_dim) +
+                        (entry == PA_ENTRY_PREFILL_INT8KV ? n * k_image_bytes(a->head_dim) : 0);
+    return (img + 255) / 256 * 256;
+}
+
+int64_t workspace_need(const pa_paged_args *a, int32_t entry) {
+    return sched_offset(a, entry) +
+           4 * attn_sched_slots(a->num_reqs, a->num_kv_heads, a->max_q_len, a->num_q_heads / a->num_kv_heads);
 }
 
 int check_workspace(const pa_paged_args *a, int32_t entry, void *ws, size_t bytes) {
@@ -170,6 +177,8 @@ int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, c
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, false, false, stream)))) return rc;
     AttnParams p = attn_params(a);
+    p.sched = (int32_t *)((char *)workspace + sched_offset(a, PA_ENTRY_PREFILL_BF16));
+    if (build && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.q = q;
     p.k = k_pool;
     p.v_img = (const char *)workspace;
@@ -198,6 +207,8 @@ int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_poo
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, true, true, stream)))) return rc;
     AttnParams p = attn_params(a);
+    p.sched = (int32_t *)((char *)workspace + sched_offset(a, PA_ENTRY_PREFILL_INT8KV));
+    if (build && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.q = q;
     p.v_img = (const char *)ip.dst;
     p.k_img = (const char *)ip.dst2;
@@ -264,6 +275,8 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8, false, stream)))) return rc;
     AttnParams p = attn_params(a);
+    p.sched = (int32_t *)((char *)workspace + sched_offset(a, PA_ENTRY_PREFILL_INT8QK));
+    if (build && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.cu_ctx = cu_ctx;
     p.q = q;
     p.k = k8;

@@ -182,8 +182,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     const int lane = tid & 63, wave = tid >> 6;
     const int lc = lane & 31, hf = lane >> 5;
 
-    // ---- work item: (request, KV head, column tile), XCD-contiguous
-    const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
+    // ---- work item: (request, KV head, column tile), from the schedule
+    const int32_t item = P.sched[blockIdx.x];
+    if (item < 0) return;
+    const uint32_t logical = (uint32_t)item;
     const int tile = (int)(logical % (uint32_t)P.tiles);
     const int rest = (int)(logical / (uint32_t)P.tiles);
     const int g = rest % P.Hkv;
@@ -612,14 +614,16 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         PA_FENCE();
 
         // P = 2^(logit - m_run) for element e = 16 kb + i of tile kt; the fp16 B
-        // operand of PV step st takes elements 8 st .. 8 st + 7
+        // operand of PV step st takes elements 8 st .. 8 st + 7.  The row sum
+        // of P is added up in phase B, which carries fewer vector instructions
+        // per MFMA (the int8-QK arm's phase A has one QK MFMA per two
+        // exponentials)
         float psum = 0.f;
         f16x8 pb[4];
         auto exp_el = [&](int e) {
             const int kb = e >> 4, i = e & 15;
             const float p = exp2_fast(fmaf(sc[kb][i], smfac, -m_run));
             sc[kb][i] = p;
-            psum += p;
             if ((e & 7) == 7) {
                 const int st = e >> 3, base = (st & 1) * 8;
 #pragma unroll
@@ -668,7 +672,6 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             for (int e = 0; e < 32; ++e) exp_el(e);
             PA_FENCE();
         }
-        l_run += psum;
         // every wave is past phase A, so K(kt+1)'s stage may take K(kt+3), and
         // every wave's K(kt+2) copies (issued before this step's V copies) have
         // landed, so phase B may read ahead into tile kt+2
@@ -699,12 +702,15 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 for (int k = j * PFQ / NB; k < (j + 1) * PFQ / NB; ++k) kout[k] = rdK(kr2, k);
             }
             pv(N0 + j);
+#pragma unroll
+            for (int e = j * 32 / NB; e < (j + 1) * 32 / NB; ++e) psum += sc[e >> 4][e & 15];
             if constexpr (NEXT) {
 #pragma unroll
                 for (int e = j * 32 / NB; e < (j + 1) * 32 / NB; ++e) post_el(e);
             }
             PA_FENCE();
         }
+        l_run += psum;
         if constexpr (NEXT) mx = max_halves(mxa) * smfac;
         // V(kt+1) (issued in phase A) and K(kt+2) (issued in the previous step's
         // phase B) have landed; the K(kt+3) copies may still be in flight
@@ -808,13 +814,126 @@ int attn_rows_per_copy(int kind, int head_dim) {
     return 1024 / (qk8 ? head_dim : 2 * head_dim);
 }
 
+// ---- work schedule.  Workgroup i of the attention grid runs on XCD i % 8
+// and takes item sched[i] (item = (request * Hkv + KV head) * tiles + column
+// tile, -1 for none).  The items of one (request, KV head) group stream the
+// same K/V tiles, so they are kept together on as few XCDs as possible (each
+// XCD's L2 then fetches a group's tiles from HBM once), while the XCDs get
+// equal numbers of items and, as far as that allows, equal work: groups in
+// decreasing order of work go to the XCD with the least work so far that has
+// room, each placement taking no more items than bring that XCD to an eighth
+// of the total work, so a group is split over XCDs only where one fills up or
+// its work exceeds that share.  Each XCD thus runs its longest groups first.  A request's work is the number of key tiles its
+// column tiles stream, plus two for a workgroup's prologue and epilogue.
+// Beyond SCHED_MAX_REQS requests or SCHED_MAX_GROUPS groups, contiguous item
+// ranges per XCD are used instead (by then many groups share an XCD).
+constexpr int SCHED_THREADS = 256;
+constexpr int SCHED_MAX_REQS = 1024;
+constexpr int SCHED_MAX_GROUPS = 1024;
+
+__global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(const AttnParams P, int32_t slots) {
+    __shared__ float work[SCHED_MAX_REQS];               // per request
+    __shared__ int ntile[SCHED_MAX_REQS];                // per request: column tiles holding columns
+    __shared__ int order[SCHED_MAX_REQS];                // requests by decreasing work
+    __shared__ int seg_item[SCHED_MAX_GROUPS + NUM_XCD]; // runs of consecutive items on one XCD:
+    __shared__ int seg_slot[SCHED_MAX_GROUPS + NUM_XCD]; //   first item, first schedule entry,
+    __shared__ int seg_len[SCHED_MAX_GROUPS + NUM_XCD];  //   length
+    __shared__ int nseg;
+    const int tid = threadIdx.x;
+    const int R = P.num_reqs, H = P.Hkv, T = P.tiles;
+    const int64_t n = (int64_t)R * H * T;
+    int32_t *sched = P.sched;
+    const int cap = slots / NUM_XCD;
+    if (R > SCHED_MAX_REQS || (int64_t)R * H > SCHED_MAX_GROUPS) {
+        for (int i = tid; i < slots; i += SCHED_THREADS) {
+            const uint32_t l = xcd_remap((uint32_t)i, (uint32_t)slots);
+            sched[i] = l < (uint64_t)n ? (int32_t)l : -1;
+        }
+        return;
+    }
+    for (int i = tid; i < slots; i += SCHED_THREADS) sched[i] = -1;
+    for (int r = tid; r < R; r += SCHED_THREADS) {
+        const int Lq = P.cu_q[r + 1] - P.cu_q[r], L = P.ctx_lens[r];
+        int nt = 0;
+        float w = 0.f;
+        if (Lq > 0 && Lq <= L) {
+            const int ncols = Lq * P.group;
+            nt = min((ncols + ATTN_COLS - 1) / ATTN_COLS, T);
+            for (int t = 0; t < nt; ++t) {
+                const int last_col = min((t + 1) * ATTN_COLS, ncols) - 1;
+                const int pos_max = P.causal ? L - Lq + last_col / P.group : L - 1;
+                w += (float)(pos_max / BN + 1) + 2.f;
+            }
+        }
+        work[r] = w;
+        ntile[r] = nt;
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += SCHED_THREADS) {
+        int rank = 0;
+        for (int o = 0; o < R; ++o) rank += (work[o] > work[r] || (work[o] == work[r] && o < r));
+        order[rank] = r;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float load[NUM_XCD];
+        int cnt[NUM_XCD];
+        for (int x = 0; x < NUM_XCD; ++x) {
+            load[x] = 0.f;
+            cnt[x] = 0;
+        }
+        float total = 0.f;
+        for (int r = 0; r < R; ++r) total += work[r];
+        const float target = total * (float)H / (float)NUM_XCD;
+        int ns = 0;
+        for (int i = 0; i < R; ++i) {
+            const int r = order[i], nt = ntile[r];
+            if (nt == 0) continue;
+            const float per = work[r] / (float)nt;
+            for (int g = 0; g < H; ++g) {
+                for (int done = 0; done < nt;) {
+                    // there is room: the items number at most slots = NUM_XCD * cap
+                    int x = -1;
+                    for (int y = 0; y < NUM_XCD; ++y)
+                        if (cnt[y] < cap && (x < 0 || load[y] < load[x])) x = y;
+                    const int room = min(nt - done, cap - cnt[x]);
+                    const int share = (int)((target - load[x]) / per + 0.5f);
+                    const int take = max(1, min(room, share));
+                    seg_item[ns] = (r * H + g) * T + done;
+                    seg_slot[ns] = cnt[x] * NUM_XCD + x;
+                    seg_len[ns] = take;
+                    ++ns;
+                    load[x] += (float)take * per;
+                    cnt[x] += take;
+                    done += take;
+                }
+            }
+        }
+        nseg = ns;
+    }
+    __syncthreads();
+    const int ns = nseg;
+    for (int sg = 0; sg < ns; ++sg)
+        for (int j = tid; j < seg_len[sg]; j += SCHED_THREADS) sched[seg_slot[sg] + j * NUM_XCD] = seg_item[sg] + j;
+}
+
+hipError_t launch_schedule(const AttnParams &p, int32_t max_q_len, hipStream_t stream) {
+    AttnParams q = p;
+    q.tiles = (int32_t)attn_col_tiles(max_q_len, p.group);
+    const int64_t slots = attn_sched_slots(p.num_reqs, p.Hkv, max_q_len, p.group);
+    if (slots <= 0) return hipSuccess;
+    if (slots > 0x7fffffff || !q.sched) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(SCHED_THREADS), 0, stream, q, (int32_t)slots);
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,
                             int32_t max_q_len, hipStream_t stream) {
     AttnParams q = p;
-    q.tiles = (int32_t)(((int64_t)max_q_len * p.group + NCOL - 1) / NCOL);
-    const int64_t nwg = (int64_t)q.tiles * p.Hkv * p.num_reqs;
+    q.tiles = (int32_t)attn_col_tiles(max_q_len, p.group);
+    const int64_t nwg = attn_sched_slots(p.num_reqs, p.Hkv, max_q_len, p.group);
     if (nwg <= 0) return hipSuccess;
-    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
+    if (nwg > 0x7fffffff || !q.sched) return hipErrorInvalidValue;
     dim3 grid((uint32_t)nwg);
     switch (kind) {
         case KIND_BF16: return launch_d<KIND_BF16>(head_dim, out_bf16, q, grid, stream);

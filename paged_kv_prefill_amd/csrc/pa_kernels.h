@@ -26,6 +26,7 @@ struct AttnParams {
     float scale_log2;           // softmax scale * log2(e)
     int32_t causal;
     int32_t tiles;              // column tiles per (request, kv head)
+    int32_t *sched;             // work schedule: item per workgroup, -1 = none (workspace)
     const void *q;
     const void *k;              // bf16 / int8 pool, or dense k8
     const void *v;              // bf16 / int8 pool
@@ -88,6 +89,8 @@ hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnPar
 // key rows per 1 KB K copy of an attention kind (fixes the tile's key order)
 int attn_rows_per_copy(int kind, int head_dim);
 hipError_t launch_images(const ImageParams &p, bool v_int8, bool k_image, hipStream_t stream);
+// the attention work schedule for these lengths (into p.sched)
+hipError_t launch_schedule(const AttnParams &p, int32_t max_q_len, hipStream_t stream);
 hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);
 hipError_t launch_k_quant(const PassParams &p, hipStream_t stream);
 hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t stream);
@@ -95,5 +98,17 @@ hipError_t launch_gather(const PassParams &p, hipStream_t stream);
 
 constexpr int ATTN_THREADS = 256;
 constexpr int ATTN_COLS = 128;   // (token, q head) columns per workgroup
+constexpr int NUM_XCD = 8;       // workgroup i runs on XCD i % 8
+// attention work items per (request, KV head): tiles of ATTN_COLS columns, a
+// column being a (chunk row, q head of the group) pair
+inline int64_t attn_col_tiles(int32_t max_q_len, int32_t group) {
+    return ((int64_t)max_q_len * group + ATTN_COLS - 1) / ATTN_COLS;
+}
+// entries of the work schedule, one per attention workgroup: the items,
+// rounded up to a whole number per XCD
+inline int64_t attn_sched_slots(int32_t num_reqs, int32_t num_kv_heads, int32_t max_q_len, int32_t group) {
+    const int64_t n = (int64_t)num_reqs * num_kv_heads * attn_col_tiles(max_q_len, group);
+    return (n + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+}
 
 }  // namespace pa

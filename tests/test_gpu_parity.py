@@ -185,8 +185,10 @@ def test_fp8_every_code(orc):
 @pytest.mark.parametrize("arm", ["bf16", "int8kv", "int8qk"])
 def test_images_ready_flag(arm):
     """PA_FLAG_IMAGES_READY on a workspace an identical call filled gives the
-    same bits; on a workspace of 0xFF bytes (NaN images) the output turns
-    non-finite, so the flag really skips the image pass."""
+    same bits; with the images overwritten by 0xFF bytes (NaN) the output turns
+    non-finite, so the flag really skips the image pass, and with the schedule
+    overwritten so (-1 entries) no output is written, so it skips the schedule
+    pass too."""
     from paged_kv_prefill_amd import ops
     g = gc()
     w = synth.make_case(120, [37, 20], [300, 133], 64, 4, 2, 128,
@@ -196,10 +198,10 @@ def test_images_ready_flag(arm):
              "int8qk": ops.PA_ENTRY_PREFILL_INT8QK}[arm]
     ks, k8 = case.run_k_passes() if arm == "int8qk" else (None, None)
 
-    def call(flags, ws):
+    def call(flags, ws, fill=float("nan")):
         p = case.paged()
         p.flags = flags
-        o = case.out()
+        o = case.out().fill_(fill)
         if arm == "bf16":
             ops.pa_prefill_bf16(p, case.q, case.k_pool, case.v_pool, o, ws=ws)
         elif arm == "int8kv":
@@ -216,6 +218,94 @@ def test_images_ready_flag(arm):
     again = call(ops.PA_FLAG_IMAGES_READY, ws)
     assert torch.isfinite(first).all().item()
     assert torch.equal(first.view(torch.int32), again.view(torch.int32))
-    poisoned = torch.full_like(ws, 0xFF)
+    off = sched_offset(w, arm)
+    poisoned = ws.clone()
+    poisoned[:off] = 0xFF                   # images only: the schedule stays valid
     skipped = call(ops.PA_FLAG_IMAGES_READY, poisoned)
     assert not torch.isfinite(skipped).all().item()
+    no_sched = ws.clone()
+    no_sched[off:] = 0xFF                   # schedule of -1 entries: no workgroup runs
+    assert (call(ops.PA_FLAG_IMAGES_READY, no_sched, fill=0.0) == 0).all().item()
+
+
+def sched_offset(w, arm):
+    """byte offset of the work schedule in an attention workspace"""
+    n = len(w.ctx_lens) * -(-int(w.ctx_lens.max()) // 64) * w.num_kv_heads
+    img = n * (144 * w.head_dim + 256) + (n * (128 * w.head_dim + 256) if arm == "int8kv" else 0)
+    return -(-img // 256) * 256
+
+
+def sched_items(w):
+    """the work items that hold columns: (request, KV head, column tile) as
+    (r * Hkv + g) * tiles + t"""
+    group = w.num_q_heads // w.num_kv_heads
+    tiles = -(-int(w.q_lens.max()) * group // 128)
+    items = []
+    for r in range(len(w.ctx_lens)):
+        nt = -(-int(w.q_lens[r]) * group // 128)
+        for g in range(w.num_kv_heads):
+            items += [(r * w.num_kv_heads + g) * tiles + t for t in range(nt)]
+    return items, tiles
+
+
+def list_makespan(sched, work):
+    """finish time of the busiest CU when each XCD (entry % 8) hands its
+    entries, in order, to whichever of its 32 CUs frees first"""
+    import heapq
+    worst = 0
+    for x in range(8):
+        cus = [0] * 32
+        for i in sched[x::8]:
+            if i >= 0:
+                heapq.heappush(cus, heapq.heappop(cus) + work(int(i)))
+        worst = max(worst, max(cus))
+    return worst
+
+
+@pytest.mark.parametrize("shape", ["one_request", "mixed_lengths"])
+def test_work_schedule(shape):
+    """The schedule lists every work item exactly once (bit-exact), keeps a
+    single request's items in the plain XCD-contiguous layout, and for eight
+    requests of very different contexts (2,048 items, several per CU) comes
+    within 15 % of the ideal finish time (total key-tile work over 256 CUs, or
+    the largest item), well ahead of the plain layout."""
+    from paged_kv_prefill_amd import ops
+    g = gc()
+    if shape == "one_request":
+        w = synth.make_case(140, [256], [700], 64, 8, 2, 64)
+    else:
+        w = synth.make_case(141, [2048] * 8, [8000, 2100, 6000, 2048, 7000, 3000, 2500, 5000],
+                            64, 16, 4, 64)
+    case = g.DevCase(w)
+    ws = ops.workspace(case.paged(), ops.PA_ENTRY_PREFILL_BF16)
+    ops.pa_prefill_bf16(case.paged(), case.q, case.k_pool, case.v_pool, case.out(), ws=ws)
+    torch.cuda.synchronize()
+    items, tiles = sched_items(w)
+    slots = -(-len(w.ctx_lens) * w.num_kv_heads * tiles // 8) * 8
+    off = sched_offset(w, "bf16")
+    sched = ws[off:off + 4 * slots].view(torch.int32).cpu().numpy()
+    listed = sched[sched >= 0]
+    assert sorted(listed.tolist()) == sorted(items)
+    assert set(sched[sched < 0].tolist()) <= {-1}
+    if shape == "one_request":
+        n = len(items)
+        base = n // 8
+        plain = [x * base + k for k in range(base) for x in range(8)]   # entry k * 8 + x
+        assert sched[:n].tolist() == plain
+    else:
+        group = w.num_q_heads // w.num_kv_heads
+        def work(item):
+            r, t = item // tiles // w.num_kv_heads, item % tiles
+            L, Lq = int(w.ctx_lens[r]), int(w.q_lens[r])
+            last = min((t + 1) * 128, Lq * group) - 1
+            return (L - Lq + last // group) // 64 + 1 + 2
+        ws_all = [work(i) for i in items]
+        ideal = max(sum(ws_all) / 256, max(ws_all))
+        n = len(sched) // 8
+        plain = np.full(len(sched), -1)
+        for x in range(8):
+            for k in range(n):
+                if x * n + k < len(w.ctx_lens) * w.num_kv_heads * tiles:
+                    plain[k * 8 + x] = x * n + k
+        got, base = list_makespan(sched, work), list_makespan(plain, work)
+        assert got <= 1.15 * ideal and got < 0.8 * base, (got, base, ideal)

@@ -107,15 +107,24 @@ def test_entry_point_specific_errors():
 def test_workspace_size_formula():
     """num_reqs * ceil(max_ctx / 64) * Hkv V^T images of 144 * D + 256 bytes
     (fp16 rows of 64 keys padded to 72), plus as many K images of 128 * D + 256
-    bytes for the int8-KV exact arm."""
+    bytes for the int8-KV exact arm, then, from the next multiple of 256 bytes,
+    the work schedule: one int32 per attention workgroup, num_reqs * Hkv *
+    ceil(max_q_len * group / 128) rounded up to a multiple of 8."""
     L = ops.lib()
+    up = lambda x, m: -(-x // m) * m
+    for kw, items in [(dict(num_reqs=3, max_ctx_len=130, num_kv_heads=2, head_dim=64), 3 * 2 * 1),
+                      (dict(num_reqs=5, max_ctx_len=300, max_q_len=100, num_kv_heads=2, head_dim=64),
+                       5 * 2 * 2)]:
+        a = _args(**kw)
+        vimg = 144 * 64 + 256
+        kimg = 128 * 64 + 256
+        n = kw["num_reqs"] * -(-kw["max_ctx_len"] // 64) * 2
+        sched = 4 * up(items, 8)
+        assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_BF16) == up(n * vimg, 256) + sched
+        assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8QK) == up(n * vimg, 256) + sched
+        assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8KV) == \
+            up(n * (vimg + kimg), 256) + sched
     a = _args(num_reqs=3, max_ctx_len=130, num_kv_heads=2, head_dim=64)
-    vimg = 144 * 64 + 256
-    kimg = 128 * 64 + 256
-    n = 3 * 3 * 2
-    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_BF16) == n * vimg
-    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8QK) == n * vimg
-    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8KV) == n * (vimg + kimg)
     assert L.pa_workspace_bytes(C.byref(a), 99) == 0
     assert L.pa_workspace_bytes(C.byref(_args(num_q_heads=3)), ops.PA_ENTRY_PREFILL_BF16) == 0
 
