@@ -123,6 +123,12 @@ int64_t sched_offset(const pa_paged_args *a, int32_t entry) {
     return (img + 255) / 256 * 256;
 }
 
+// the schedule in the workspace; none for a single request, whose schedule
+// is the attention kernel's default item order
+int32_t *schedule_ptr(const pa_paged_args *a, int32_t entry, void *ws) {
+    return a->num_reqs > 1 ? (int32_t *)((char *)ws + sched_offset(a, entry)) : nullptr;
+}
+
 int64_t workspace_need(const pa_paged_args *a, int32_t entry) {
     return sched_offset(a, entry) +
            4 * attn_sched_slots(a->num_reqs, a->num_kv_heads, a->max_q_len, a->num_q_heads / a->num_kv_heads);
@@ -177,8 +183,8 @@ int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, c
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, false, false, stream)))) return rc;
     AttnParams p = attn_params(a);
-    p.sched = (int32_t *)((char *)workspace + sched_offset(a, PA_ENTRY_PREFILL_BF16));
-    if (build && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_BF16, workspace);
+    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.q = q;
     p.k = k_pool;
     p.v_img = (const char *)workspace;
@@ -207,8 +213,8 @@ int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_poo
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, true, true, stream)))) return rc;
     AttnParams p = attn_params(a);
-    p.sched = (int32_t *)((char *)workspace + sched_offset(a, PA_ENTRY_PREFILL_INT8KV));
-    if (build && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_INT8KV, workspace);
+    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.q = q;
     p.v_img = (const char *)ip.dst;
     p.k_img = (const char *)ip.dst2;
@@ -275,8 +281,8 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8, false, stream)))) return rc;
     AttnParams p = attn_params(a);
-    p.sched = (int32_t *)((char *)workspace + sched_offset(a, PA_ENTRY_PREFILL_INT8QK));
-    if (build && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_INT8QK, workspace);
+    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.cu_ctx = cu_ctx;
     p.q = q;
     p.k = k8;

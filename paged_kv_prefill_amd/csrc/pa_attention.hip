@@ -182,8 +182,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     const int lane = tid & 63, wave = tid >> 6;
     const int lc = lane & 31, hf = lane >> 5;
 
-    // ---- work item: (request, KV head, column tile), from the schedule
-    const int32_t item = P.sched[blockIdx.x];
+    // ---- work item: (request, KV head, column tile), from the schedule (a
+    // single request: XCD-contiguous item ranges, which is what the schedule
+    // would be)
+    const int32_t item = P.sched ? P.sched[blockIdx.x] : (int32_t)xcd_remap(blockIdx.x, gridDim.x);
     if (item < 0) return;
     const uint32_t logical = (uint32_t)item;
     const int tile = (int)(logical % (uint32_t)P.tiles);
@@ -831,13 +833,25 @@ constexpr int SCHED_THREADS = 256;
 constexpr int SCHED_MAX_REQS = 1024;
 constexpr int SCHED_MAX_GROUPS = 1024;
 
+// At most SCHED_MAX_GROUPS + SEG_EXTRA runs: a placement splits a group only
+// where an XCD fills up (at most once per XCD) or reaches its share of the
+// work (at most twice per XCD: the share rounds to whole items).
+constexpr int SEG_EXTRA = 3 * NUM_XCD;
+
+__device__ void plain_schedule(int32_t *sched, int slots, int64_t n) {
+    for (int i = threadIdx.x; i < slots; i += SCHED_THREADS) {
+        const uint32_t l = xcd_remap((uint32_t)i, (uint32_t)slots);
+        sched[i] = l < (uint64_t)n ? (int32_t)l : -1;
+    }
+}
+
 __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(const AttnParams P, int32_t slots) {
-    __shared__ float work[SCHED_MAX_REQS];               // per request
-    __shared__ int ntile[SCHED_MAX_REQS];                // per request: column tiles holding columns
-    __shared__ int order[SCHED_MAX_REQS];                // requests by decreasing work
-    __shared__ int seg_item[SCHED_MAX_GROUPS + NUM_XCD]; // runs of consecutive items on one XCD:
-    __shared__ int seg_slot[SCHED_MAX_GROUPS + NUM_XCD]; //   first item, first schedule entry,
-    __shared__ int seg_len[SCHED_MAX_GROUPS + NUM_XCD];  //   length
+    __shared__ float work[SCHED_MAX_REQS];                 // per request
+    __shared__ int ntile[SCHED_MAX_REQS];                  // per request: column tiles holding columns
+    __shared__ int order[SCHED_MAX_REQS];                  // requests by decreasing work
+    __shared__ int seg_item[SCHED_MAX_GROUPS + SEG_EXTRA]; // runs of consecutive items on one XCD:
+    __shared__ int seg_slot[SCHED_MAX_GROUPS + SEG_EXTRA]; //   first item, first schedule entry,
+    __shared__ int seg_len[SCHED_MAX_GROUPS + SEG_EXTRA];  //   length
     __shared__ int nseg;
     const int tid = threadIdx.x;
     const int R = P.num_reqs, H = P.Hkv, T = P.tiles;
@@ -845,28 +859,25 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(const AttnParams P
     int32_t *sched = P.sched;
     const int cap = slots / NUM_XCD;
     if (R > SCHED_MAX_REQS || (int64_t)R * H > SCHED_MAX_GROUPS) {
-        for (int i = tid; i < slots; i += SCHED_THREADS) {
-            const uint32_t l = xcd_remap((uint32_t)i, (uint32_t)slots);
-            sched[i] = l < (uint64_t)n ? (int32_t)l : -1;
-        }
+        plain_schedule(sched, slots, n);
         return;
     }
     for (int i = tid; i < slots; i += SCHED_THREADS) sched[i] = -1;
     for (int r = tid; r < R; r += SCHED_THREADS) {
         const int Lq = P.cu_q[r + 1] - P.cu_q[r], L = P.ctx_lens[r];
-        int nt = 0;
-        float w = 0.f;
-        if (Lq > 0 && Lq <= L) {
-            const int ncols = Lq * P.group;
-            nt = min((ncols + ATTN_COLS - 1) / ATTN_COLS, T);
-            for (int t = 0; t < nt; ++t) {
-                const int last_col = min((t + 1) * ATTN_COLS, ncols) - 1;
-                const int pos_max = P.causal ? L - Lq + last_col / P.group : L - 1;
-                w += (float)(pos_max / BN + 1) + 2.f;
-            }
-        }
-        work[r] = w;
-        ntile[r] = nt;
+        ntile[r] = (Lq > 0 && Lq <= L) ? min((Lq * P.group + ATTN_COLS - 1) / ATTN_COLS, T) : 0;
+        work[r] = 0.f;
+    }
+    __syncthreads();
+    // key tiles of each (request, column tile), one pair per thread (integer
+    // sums, exact in fp32 whatever the order of the additions)
+    for (int i = tid; i < R * T; i += SCHED_THREADS) {
+        const int r = i / T, t = i - r * T;
+        if (t >= ntile[r]) continue;
+        const int Lq = P.cu_q[r + 1] - P.cu_q[r], L = P.ctx_lens[r];
+        const int last_col = min((t + 1) * ATTN_COLS, Lq * P.group) - 1;
+        const int pos_max = P.causal ? L - Lq + last_col / P.group : L - 1;
+        atomicAdd(&work[r], (float)(pos_max / BN + 1) + 2.f);
     }
     __syncthreads();
     for (int r = tid; r < R; r += SCHED_THREADS) {
@@ -876,8 +887,11 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(const AttnParams P
     }
     __syncthreads();
     if (tid == 0) {
+        // per-XCD work and item counts, in registers: every index below is a
+        // compile-time constant once the loops over the XCDs are unrolled
         float load[NUM_XCD];
         int cnt[NUM_XCD];
+#pragma unroll
         for (int x = 0; x < NUM_XCD; ++x) {
             load[x] = 0.f;
             cnt[x] = 0;
@@ -886,25 +900,38 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(const AttnParams P
         for (int r = 0; r < R; ++r) total += work[r];
         const float target = total * (float)H / (float)NUM_XCD;
         int ns = 0;
-        for (int i = 0; i < R; ++i) {
+        for (int i = 0; i < R && ns >= 0; ++i) {
             const int r = order[i], nt = ntile[r];
             if (nt == 0) continue;
             const float per = work[r] / (float)nt;
-            for (int g = 0; g < H; ++g) {
+            for (int g = 0; g < H && ns >= 0; ++g) {
                 for (int done = 0; done < nt;) {
                     // there is room: the items number at most slots = NUM_XCD * cap
-                    int x = -1;
+                    int x = -1, cx = 0;
+                    float lx = 0.f;
+#pragma unroll
                     for (int y = 0; y < NUM_XCD; ++y)
-                        if (cnt[y] < cap && (x < 0 || load[y] < load[x])) x = y;
-                    const int room = min(nt - done, cap - cnt[x]);
-                    const int share = (int)((target - load[x]) / per + 0.5f);
-                    const int take = max(1, min(room, share));
+                        if (cnt[y] < cap && (x < 0 || load[y] < lx)) {
+                            x = y;
+                            lx = load[y];
+                            cx = cnt[y];
+                        }
+                    const int room = min(nt - done, cap - cx);
+                    const int take = lx < target ? max(1, min(room, (int)((target - lx) / per + 0.5f))) : room;
+                    if (ns == SCHED_MAX_GROUPS + SEG_EXTRA) {   // not reached (see SEG_EXTRA)
+                        ns = -1;
+                        break;
+                    }
                     seg_item[ns] = (r * H + g) * T + done;
-                    seg_slot[ns] = cnt[x] * NUM_XCD + x;
+                    seg_slot[ns] = cx * NUM_XCD + x;
                     seg_len[ns] = take;
                     ++ns;
-                    load[x] += (float)take * per;
-                    cnt[x] += take;
+#pragma unroll
+                    for (int y = 0; y < NUM_XCD; ++y)
+                        if (y == x) {
+                            load[y] += (float)take * per;
+                            cnt[y] += take;
+                        }
                     done += take;
                 }
             }
@@ -913,6 +940,10 @@ __global__ __launch_bounds__(SCHED_THREADS) void sched_kernel(const AttnParams P
     }
     __syncthreads();
     const int ns = nseg;
+    if (ns < 0) {
+        plain_schedule(sched, slots, n);
+        return;
+    }
     for (int sg = 0; sg < ns; ++sg)
         for (int j = tid; j < seg_len[sg]; j += SCHED_THREADS) sched[seg_slot[sg] + j * NUM_XCD] = seg_item[sg] + j;
 }
@@ -933,7 +964,7 @@ hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnPar
     q.tiles = (int32_t)attn_col_tiles(max_q_len, p.group);
     const int64_t nwg = attn_sched_slots(p.num_reqs, p.Hkv, max_q_len, p.group);
     if (nwg <= 0) return hipSuccess;
-    if (nwg > 0x7fffffff || !q.sched) return hipErrorInvalidValue;
+    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((uint32_t)nwg);
     switch (kind) {
         case KIND_BF16: return launch_d<KIND_BF16>(head_dim, out_bf16, q, grid, stream);

@@ -262,17 +262,18 @@ def list_makespan(sched, work):
     return worst
 
 
-@pytest.mark.parametrize("shape", ["one_request", "mixed_lengths"])
+@pytest.mark.parametrize("shape", ["equal_requests", "mixed_lengths"])
 def test_work_schedule(shape):
-    """The schedule lists every work item exactly once (bit-exact), keeps a
-    single request's items in the plain XCD-contiguous layout, and for eight
+    """The schedule lists every work item exactly once (bit-exact), keeps
+    requests of equal lengths in the plain XCD-contiguous layout (the one a
+    single request gets without a schedule), and for eight
     requests of very different contexts (2,048 items, several per CU) comes
     within 15 % of the ideal finish time (total key-tile work over 256 CUs, or
     the largest item), well ahead of the plain layout."""
     from paged_kv_prefill_amd import ops
     g = gc()
-    if shape == "one_request":
-        w = synth.make_case(140, [256], [700], 64, 8, 2, 64)
+    if shape == "equal_requests":
+        w = synth.make_case(140, [256, 256], [700, 700], 64, 8, 2, 64)
     else:
         w = synth.make_case(141, [2048] * 8, [8000, 2100, 6000, 2048, 7000, 3000, 2500, 5000],
                             64, 16, 4, 64)
@@ -287,7 +288,7 @@ def test_work_schedule(shape):
     listed = sched[sched >= 0]
     assert sorted(listed.tolist()) == sorted(items)
     assert set(sched[sched < 0].tolist()) <= {-1}
-    if shape == "one_request":
+    if shape == "equal_requests":
         n = len(items)
         base = n // 8
         plain = [x * base + k for k in range(base) for x in range(8)]   # entry k * 8 + x
