@@ -13,7 +13,9 @@ are seeded synthetic N(0,1) bf16 values, resident in HBM before timing starts.
 
 Printed: one JSON line with the headline tokens/s (whole calls), the roofline
 of the attention kernel alone (algorithmic FLOPs per launch / its measured
-launch time, against the bf16 dense MFMA peak; timed with the image pass
+launch time, against the bf16 dense MFMA peak, and also against the MFMA
+throughput the chip sustains on the same instruction shape with no other work
+(pa_peak_probe, measured in the same run); timed with the image pass
 skipped via PA_FLAG_IMAGES_READY), its HBM bytes per launch from the committed
 counter profile when that was taken on this build, the CPU oracle's rate on a
 bounded sample, and the other arms (int8 KV exact-QK, int8-QK with its two K
@@ -139,6 +141,22 @@ def time_launches(fns, steps: int, warmup: int):
     return per, wall
 
 
+def measured_peaks(reps: int = 20):
+    """Sustained MFMA throughput of the chip on the attention's MFMA shapes
+    (pa_peak_probe: eight workgroups per CU, register operands, no other
+    work), right after the attention timing so the thermal state is alike.
+    Returns {"bf16": TFLOP/s, "int8": TOP/s}."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = 8 * cus, 250
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=DEV)
+    res = {}
+    for name, dt in (("bf16", ops.PA_DTYPE_BF16), ("int8", ops.PA_DTYPE_INT8)):
+        (ms,), _ = time_launches([lambda dt=dt: ops.pa_peak_probe(dt, wgs, iters, out)], reps, 3)
+        ops_per = wgs * 4 * iters * 32 * ops.PROBE_FLOP_PER_MFMA[dt]
+        res[name] = ops_per / ms * 1e-9
+    return res
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, block_table, target_s: float = 12.0):
     """The oracle as it stands, on the host cores, over a sample of chunk rows
@@ -210,7 +228,7 @@ def traffic_from_profile(build_id: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
-def arm_int8(steps, warmup):
+def arm_int8(steps, warmup, peaks=None):
     w = synth.config_bigpool_int8()
     P = Pools(w, w.extra["top_block_table"])
     p = P.paged()
@@ -241,6 +259,8 @@ def arm_int8(steps, warmup):
                     "tokens_per_s": chunk / (t_stats + t_quant + t_qk8) * 1e3,
                     "attention_tops": fl / t_qk8 * 1e-9,
                     "mfma_frac_blended_peak": fl / t_qk8 * 1e-9 / blended,
+                    **({"mfma_frac_blended_measured": fl / t_qk8 * 1e-9 /
+                        (1.0 / (0.5 / peaks["int8"] + 0.5 / peaks["bf16"]))} if peaks else {}),
                     "k_stats": {"ms": t_stats, "gbs": stats_bytes / t_stats * 1e-6,
                                 "hbm_frac": stats_bytes / t_stats * 1e-6 / PEAK_HBM_GBS},
                     "k_quant": {"ms": t_quant, "gbs": quant_bytes / t_quant * 1e-6,
@@ -323,6 +343,7 @@ def main():
                                                                     args.calib_copy)
     chunk = int(w.q_lens.sum())
     achieved = flops / ms * 1e-9                     # TFLOP/s, attention kernel alone
+    peaks = measured_peaks()
     line = {
         "metric": METRIC,
         "value": chunk / (wall * 1e-3),
@@ -344,14 +365,16 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic_from_profile(ops.build_id()),
                      "kernel": "attn_kernel<256, bf16 KV>", "kernel_ms": ms,
-                     "call_ms": ms_call, "flops_per_launch": flops},
+                     "call_ms": ms_call, "flops_per_launch": flops,
+                     "measured_peak": peaks["bf16"], "frac_of_measured": achieved / peaks["bf16"],
+                     "measured_peak_int8": peaks["int8"]},
         "library": ops.build_id(),
     }
     if calib_bytes is not None:
         line["calib_copy_bytes"] = calib_bytes
     if args.arms == "all":
         arms = {}
-        arms.update(arm_int8(args.steps, args.warmup))
+        arms.update(arm_int8(args.steps, args.warmup, peaks))
         torch.cuda.empty_cache()
         arms.update(arm_fp8(args.steps, args.warmup))
         torch.cuda.empty_cache()

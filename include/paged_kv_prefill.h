@@ -218,6 +218,21 @@ int pa_fp8_dense_dequant(const pa_paged_args *args, const uint8_t *k_pool,
 int pa_gather_kv(const pa_paged_args *args, const void *pool, int32_t elem_bytes,
                  const int32_t *cu_ctx, void *dense, hipStream_t stream);
 
+/*
+ * pa_peak_probe -- measurement export: the MFMA throughput the chip sustains
+ * on the attention's own instruction shapes, to report utilisation against
+ * beside the data-sheet peak.  Launches `workgroups` workgroups of 256
+ * threads (one wave per SIMD); every wave issues iters * 32 independent MFMAs
+ * on register operands with no other work: dtype PA_DTYPE_BF16 runs
+ * v_mfma_f32_32x32x16_bf16 (32,768 FLOP each), PA_DTYPE_INT8
+ * v_mfma_i32_32x32x32_i8 (65,536 ops each).  Writes one float per thread to
+ * out (device, workgroups * 256 floats) so the work is kept.  The caller
+ * times it on `stream`.
+ * Errors: PA_ERR_UNSUPPORTED for another dtype, PA_ERR_NULL for out,
+ * PA_ERR_SHAPE for workgroups outside [1, 2^20] or iters outside [1, 2^24].
+ */
+int pa_peak_probe(int32_t dtype, int32_t workgroups, int32_t iters, float *out, hipStream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *pa_status_string(int32_t status);
 

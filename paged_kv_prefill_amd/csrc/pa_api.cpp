@@ -337,6 +337,13 @@ int pa_gather_kv(const pa_paged_args *a, const void *pool, int32_t elem_bytes,
     return launched(launch_gather(p, stream));
 }
 
+int pa_peak_probe(int32_t dtype, int32_t workgroups, int32_t iters, float *out, hipStream_t stream) {
+    if (dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_INT8) return PA_ERR_UNSUPPORTED;
+    if (!out) return PA_ERR_NULL;
+    if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24)) return PA_ERR_SHAPE;
+    return launched(launch_probe(dtype == PA_DTYPE_INT8, workgroups, iters, out, stream));
+}
+
 const char *pa_status_string(int32_t status) {
     switch (status) {
         case PA_OK: return "ok";

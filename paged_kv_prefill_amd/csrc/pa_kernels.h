@@ -95,6 +95,7 @@ hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);
 hipError_t launch_k_quant(const PassParams &p, hipStream_t stream);
 hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t stream);
 hipError_t launch_gather(const PassParams &p, hipStream_t stream);
+hipError_t launch_probe(bool int8, int32_t workgroups, int32_t iters, float *out, hipStream_t stream);
 
 constexpr int ATTN_THREADS = 256;
 constexpr int ATTN_COLS = 128;   // (token, q head) columns per workgroup

@@ -25,7 +25,7 @@ PA_FLAG_IMAGES_READY = 1
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_k_stats", "pa_k_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_gather_kv",
-                "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
+                "pa_peak_probe", "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
 
 
 class PagedArgs(C.Structure):
@@ -67,6 +67,7 @@ def lib():
             "pa_prefill_int8qk": [pa, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
             "pa_fp8_dense_dequant": [pa, vp, vp, vp, vp, i32, vp, vp, vp],
             "pa_gather_kv": [pa, vp, i32, vp, vp, vp],
+            "pa_peak_probe": [i32, i32, i32, vp, vp],
         }
         for name, argt in sig.items():
             fn = getattr(L, name)
@@ -237,6 +238,17 @@ def pa_gather_kv(p: Paged, pool, cu_ctx, dense, stream=None):
     _check(lib().pa_gather_kv(C.byref(a), _p(pool), pool.element_size(), _p(cu_ctx), _p(dense),
                               _stream(stream)), "pa_gather_kv")
     return dense
+
+
+def pa_peak_probe(dtype: int, workgroups: int, iters: int, out, stream=None):
+    """MFMA-only throughput probe (measurement): every wave of `workgroups`
+    workgroups issues iters * 32 MFMAs; out holds workgroups * 256 floats."""
+    _check(lib().pa_peak_probe(int(dtype), int(workgroups), int(iters), _p(out), _stream(stream)),
+           "pa_peak_probe")
+    return out
+
+
+PROBE_FLOP_PER_MFMA = {PA_DTYPE_BF16: 32 * 32 * 16 * 2, PA_DTYPE_INT8: 32 * 32 * 32 * 2}
 
 
 def scratch_view(p: Paged, max_seq: int, device) -> Paged:

@@ -310,3 +310,18 @@ def test_work_schedule(shape):
                     plain[k * 8 + x] = x * n + k
         got, base = list_makespan(sched, work), list_makespan(plain, work)
         assert got <= 1.15 * ideal and got < 0.8 * base, (got, base, ideal)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "int8"])
+def test_peak_probe_runs(dtype):
+    """The MFMA probe (measurement export) runs, writes every output, finite,
+    and the same values on a second call."""
+    from paged_kv_prefill_amd import ops
+    dt = ops.PA_DTYPE_BF16 if dtype == "bf16" else ops.PA_DTYPE_INT8
+    out = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    ops.pa_peak_probe(dt, 4, 3, out)
+    first = out.clone()
+    ops.pa_peak_probe(dt, 4, 3, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(first).all().item()
+    assert torch.equal(first, out)

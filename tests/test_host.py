@@ -102,6 +102,10 @@ def test_entry_point_specific_errors():
     assert L.pa_fp8_dense_dequant(C.byref(a), p, p, p, p, 8, p, p, None) == ops.PA_ERR_SHAPE
     assert L.pa_fp8_dense_dequant(C.byref(a), p, p, None, p, 16, p, p, None) == ops.PA_ERR_NULL
     assert L.pa_gather_kv(C.byref(a), p, 4, p, p, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_peak_probe(ops.PA_DTYPE_F32, 1, 1, p, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_peak_probe(ops.PA_DTYPE_BF16, 1, 1, None, None) == ops.PA_ERR_NULL
+    assert L.pa_peak_probe(ops.PA_DTYPE_INT8, 0, 1, p, None) == ops.PA_ERR_SHAPE
+    assert L.pa_peak_probe(ops.PA_DTYPE_INT8, 1, 1 << 25, p, None) == ops.PA_ERR_SHAPE
 
 
 def test_workspace_size_formula():
