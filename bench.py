@@ -372,13 +372,18 @@ def main():
     }
     if calib_bytes is not None:
         line["calib_copy_bytes"] = calib_bytes
+    progress = lambda what: print(f"bench: {what} done", file=sys.stderr, flush=True)
+    progress("headline arm and MFMA probe")
     if args.arms == "all":
         arms = {}
         arms.update(arm_int8(args.steps, args.warmup, peaks))
+        progress("int8 arms")
         torch.cuda.empty_cache()
         arms.update(arm_fp8(args.steps, args.warmup))
+        progress("fp8 arm")
         torch.cuda.empty_cache()
         arms.update(arm_batched(args.steps, args.warmup))
+        progress("batched arm")
         line["arms"] = arms
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, top)
