@@ -48,6 +48,10 @@ def load(path: str | None = None):
         [vp, i64, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, f32, i32, i32,
          u16p, vp, vp, vp, vp, i64, i64, i32p, i64, i32, f64p])
     lib.oracle_prefill.restype = i32
+    lib.oracle_prefill_lse.argtypes = (
+        [vp, i64, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, f32, i32, i32,
+         u16p, vp, vp, vp, vp, i64, i64, i32p, i64, vp, vp, i32, f64p, f64p])
+    lib.oracle_prefill_lse.restype = i32
     lib.oracle_prefill_int8qk.argtypes = (
         [vp, i64, i32p, i32p, i32p, i32, i32, i32, i32, i32, i64, i64, i64, f32, i32, i32,
          u16p, i8p, f32p, vp, vp, i64, i64, i32p, i64, i32, f64p])
@@ -110,6 +114,40 @@ def prefill(block_table, cu_q_lens, ctx_lens, q, k_pool, v_pool, softmax_scale,
     if rc != 0:
         raise ValueError(f"oracle_prefill failed ({rc})")
     return out
+
+
+def prefill_lse(block_table, cu_q_lens, ctx_lens, q, k_pool, v_pool, softmax_scale,
+                num_kv_heads=None, causal=True, k_scales=None, v_scales=None, rows=None,
+                key_lo=None, key_hi=None, threads=0, lib=None):
+    """Attention of the listed chunk rows over keys [key_lo, key_hi) (per listed
+    row; None = unrestricted) intersected with each row's causal keys, and the
+    natural-log log-sum-exp of the scaled logits over those keys.  Returns
+    (float64 [len(rows), Hq, D], float64 [len(rows), Hq]); rows with no key
+    give O = 0 and lse = -inf."""
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    cu_q = np.ascontiguousarray(cu_q_lens, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    nb, bs, hkv, d = k_pool.shape
+    hq = q.shape[1]
+    if rows is None:
+        rows = np.arange(int(cu_q[-1]), dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    lo = None if key_lo is None else np.ascontiguousarray(np.broadcast_to(key_lo, rows.shape), dtype=np.int32)
+    hi = None if key_hi is None else np.ascontiguousarray(np.broadcast_to(key_hi, rows.shape), dtype=np.int32)
+    out = np.empty((len(rows), hq, d), dtype=np.float64)
+    lse = np.empty((len(rows), hq), dtype=np.float64)
+    kind = KV_INT8 if k_pool.dtype == np.int8 else KV_BF16
+    ssb, sst = (bs * hkv, hkv) if kind == KV_INT8 else (0, 0)
+    sb, st, sh = _pool_strides(k_pool)
+    rc = lib.oracle_prefill_lse(_ptr(bt), bt.shape[1], cu_q, ctx, len(ctx), bs, hq, hkv, d,
+                                sb, st, sh, float(softmax_scale), int(bool(causal)), kind,
+                                np.ascontiguousarray(q), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(k_scales), _ptr(v_scales), ssb, sst, rows, len(rows),
+                                _ptr(lo), _ptr(hi), int(threads), out, lse)
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_lse failed ({rc})")
+    return out, lse
 
 
 def prefill_int8qk(block_table, cu_q_lens, ctx_lens, q, k8, ks, v_pool, softmax_scale,

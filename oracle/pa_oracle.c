@@ -26,6 +26,15 @@
  *    K_j / V_j are the stored values: bf16 exactly, or code * scale (exact in
  *    double) for an int8 per-token-head pool.
  *
+ *  - Key ranges and the log-sum-exp (vllm.cpp PR #3360, "What changed": the
+ *    bf16 prefill runs on a split-KV kernel; HyperQwen PR #91: the verify
+ *    attention computes partial results that a combine step merges).  For a
+ *    subset of a row's keys the oracle also returns
+ *        lse = log sum_j exp(s_j)
+ *    in double precision; this is the plain definition of the softmax
+ *    normaliser, through which attention over disjoint key ranges merges
+ *    exactly into attention over their union.
+ *
  *  - K statistics and K quantisation of the int8 prefill (HyperQwen PR #109:
  *    the stats kernel, then the quant kernel that writes int8 K by position):
  *        ks[t, g]   = max_d |x[t, g, d]| / 127            (fp32 division)
@@ -146,17 +155,24 @@ int oracle_max_threads(void) {
 }
 
 /* Attention for the listed query rows (global row indices into q / the chunk
- * concatenation).  out is [num_rows, num_q_heads, head_dim] doubles. */
-int oracle_prefill(const int32_t *block_table, int64_t stride_bt,
-                   const int32_t *cu_q_lens, const int32_t *ctx_lens, int32_t num_reqs,
-                   int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
-                   int32_t head_dim, int64_t stride_block, int64_t stride_tok,
-                   int64_t stride_head, float softmax_scale, int32_t causal,
-                   int32_t kv_kind, const uint16_t *q, const void *k_pool,
-                   const void *v_pool, const float *k_scales, const float *v_scales,
-                   int64_t stride_sblock, int64_t stride_stok,
-                   const int32_t *rows, int64_t num_rows, int32_t num_threads,
-                   double *out) {
+ * concatenation) over the keys j in [key_lo[k], key_hi[k]) intersected with
+ * the row's own keys 0..p (0..L-1 when not causal), for listed row k; NULL
+ * bounds mean no restriction.  out is [num_rows, num_q_heads, head_dim]
+ * doubles; lse (may be NULL) is [num_rows, num_q_heads], the natural log of
+ * sum_j exp(s_j) over the same keys, -inf with out = 0 when no key remains.
+ * The log-sum-exp is what lets attention over disjoint key ranges be merged:
+ * O = sum_k exp(lse_k - lse) O_k with lse = log sum_k exp(lse_k). */
+static int prefill_range(const int32_t *block_table, int64_t stride_bt,
+                         const int32_t *cu_q_lens, const int32_t *ctx_lens, int32_t num_reqs,
+                         int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int64_t stride_block, int64_t stride_tok,
+                         int64_t stride_head, float softmax_scale, int32_t causal,
+                         int32_t kv_kind, const uint16_t *q, const void *k_pool,
+                         const void *v_pool, const float *k_scales, const float *v_scales,
+                         int64_t stride_sblock, int64_t stride_stok,
+                         const int32_t *rows, int64_t num_rows, const int32_t *key_lo,
+                         const int32_t *key_hi, int32_t num_threads, double *out,
+                         double *lse) {
     if (num_q_heads % num_kv_heads != 0 || block_size < 1 || head_dim < 1)
         return -1;
     paged_view pv = {block_table, stride_bt, block_size, stride_block, stride_tok, stride_head};
@@ -186,12 +202,15 @@ int oracle_prefill(const int32_t *block_table, int64_t stride_bt,
             int64_t i = row - cu_q_lens[r];
             int64_t p = L - qlen + i;                         /* absolute position */
             int64_t nkeys = causal ? p + 1 : L;
+            int64_t j0 = 0, j1 = nkeys;
+            if (key_lo && key_lo[w / num_q_heads] > j0) j0 = key_lo[w / num_q_heads];
+            if (key_hi && key_hi[w / num_q_heads] < j1) j1 = key_hi[w / num_q_heads];
             int g = h / group;
             for (int d = 0; d < D; ++d)
                 qv[d] = (double)bf16_bits_to_f32(q[(row * num_q_heads + h) * (int64_t)D + d]);
             /* pass 1: logits and their maximum */
             double m = -INFINITY;
-            for (int64_t j = 0; j < nkeys; ++j) {
+            for (int64_t j = j0; j < j1; ++j) {
                 int64_t off = paged_offset(&pv, r, j, g);
                 double dot = 0.0;
                 if (kv_kind == KV_BF16) {
@@ -208,7 +227,7 @@ int oracle_prefill(const int32_t *block_table, int64_t stride_bt,
             /* pass 2: exp, sum, and the weighted sum of V */
             double l = 0.0;
             for (int d = 0; d < D; ++d) acc[d] = 0.0;
-            for (int64_t j = 0; j < nkeys; ++j) {
+            for (int64_t j = j0; j < j1; ++j) {
                 double e = exp(s[j] - m);
                 l += e;
                 int64_t off = paged_offset(&pv, r, j, g);
@@ -221,13 +240,49 @@ int oracle_prefill(const int32_t *block_table, int64_t stride_bt,
                     for (int d = 0; d < D; ++d) acc[d] += e * ((double)vp[d] * sc);
                 }
             }
-            for (int d = 0; d < D; ++d) o[d] = nkeys > 0 ? acc[d] / l : 0.0;
+            for (int d = 0; d < D; ++d) o[d] = j1 > j0 ? acc[d] / l : 0.0;
+            if (lse) lse[w] = j1 > j0 ? m + log(l) : -INFINITY;
         }
         free(s);
         free(qv);
         free(acc);
     }
     return bad ? -2 : 0;
+}
+
+int oracle_prefill(const int32_t *block_table, int64_t stride_bt,
+                   const int32_t *cu_q_lens, const int32_t *ctx_lens, int32_t num_reqs,
+                   int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int64_t stride_block, int64_t stride_tok,
+                   int64_t stride_head, float softmax_scale, int32_t causal,
+                   int32_t kv_kind, const uint16_t *q, const void *k_pool,
+                   const void *v_pool, const float *k_scales, const float *v_scales,
+                   int64_t stride_sblock, int64_t stride_stok,
+                   const int32_t *rows, int64_t num_rows, int32_t num_threads,
+                   double *out) {
+    return prefill_range(block_table, stride_bt, cu_q_lens, ctx_lens, num_reqs, block_size,
+                         num_q_heads, num_kv_heads, head_dim, stride_block, stride_tok,
+                         stride_head, softmax_scale, causal, kv_kind, q, k_pool, v_pool,
+                         k_scales, v_scales, stride_sblock, stride_stok, rows, num_rows,
+                         NULL, NULL, num_threads, out, NULL);
+}
+
+/* The same with key bounds per listed row and the log-sum-exp (see above). */
+int oracle_prefill_lse(const int32_t *block_table, int64_t stride_bt,
+                       const int32_t *cu_q_lens, const int32_t *ctx_lens, int32_t num_reqs,
+                       int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int64_t stride_block, int64_t stride_tok,
+                       int64_t stride_head, float softmax_scale, int32_t causal,
+                       int32_t kv_kind, const uint16_t *q, const void *k_pool,
+                       const void *v_pool, const float *k_scales, const float *v_scales,
+                       int64_t stride_sblock, int64_t stride_stok,
+                       const int32_t *rows, int64_t num_rows, const int32_t *key_lo,
+                       const int32_t *key_hi, int32_t num_threads, double *out, double *lse) {
+    return prefill_range(block_table, stride_bt, cu_q_lens, ctx_lens, num_reqs, block_size,
+                         num_q_heads, num_kv_heads, head_dim, stride_block, stride_tok,
+                         stride_head, softmax_scale, causal, kv_kind, q, k_pool, v_pool,
+                         k_scales, v_scales, stride_sblock, stride_stok, rows, num_rows,
+                         key_lo, key_hi, num_threads, out, lse);
 }
 
 /* ------------------------------------------------------------ int8-QK arm */

@@ -205,6 +205,101 @@ def test_gqa_equals_mha_with_replicated_kv(orc):
     assert np.array_equal(out, out_mha)
 
 
+# ------------------------------------------------------------------ key ranges, log-sum-exp
+def run_oracle_lse(orc, w, key_lo=None, key_hi=None, rows=None, causal=True):
+    pools = synth.host_pools(w)
+    return orc.prefill_lse(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
+                           w.softmax_scale, causal=causal, k_scales=pools.get("k_scales"),
+                           v_scales=pools.get("v_scales"), rows=rows, key_lo=key_lo,
+                           key_hi=key_hi)
+
+
+def brute_logits(w, r, h):
+    """float64 logits [Lq, L] of request r, q head h, from the dense K by numpy
+    products (no causal mask applied)."""
+    K = dense_values(w, "k")
+    Q = dec_bf16(w.q)
+    cq, cc = w.cu_q_lens, w.cu_ctx_lens
+    g = h // (w.num_q_heads // w.num_kv_heads)
+    return w.softmax_scale * (Q[cq[r]:cq[r + 1], h] @ K[cc[r]:cc[r + 1], g].T)
+
+
+def test_lse_matches_brute_force_logsumexp(orc):
+    """lse = log sum_j exp(s_j) over the row's causal keys, against scipy's
+    logsumexp of numpy-computed logits; O is unchanged by asking for it."""
+    from scipy.special import logsumexp
+    w = synth.make_case(21, [7, 3], [30, 11], 4, 4, 2, 64)
+    out, lse = run_oracle_lse(orc, w)
+    assert np.array_equal(out, run_oracle(orc, w))
+    for r in range(w.num_reqs):
+        L, Lq = int(w.ctx_lens[r]), int(w.q_lens[r])
+        for h in range(w.num_q_heads):
+            s = brute_logits(w, r, h)
+            for i in range(Lq):
+                p = L - Lq + i
+                ref = logsumexp(s[i, : p + 1])
+                assert abs(lse[w.cu_q_lens[r] + i, h] - ref) < 1e-12
+
+
+def test_lse_zero_query_is_log_of_key_count(orc):
+    """q = 0 makes every logit 0, so lse = log(number of keys in the range)."""
+    w = synth.make_case(22, [6], [20], 4, 4, 2, 64)
+    w.q = np.zeros_like(w.q)
+    lo = np.array([3, 0, 5, 9, 14, 2], np.int32)
+    hi = np.array([10, 15, 16, 12, 40, 3], np.int32)
+    out, lse = run_oracle_lse(orc, w, key_lo=lo, key_hi=hi)
+    V = dense_values(w, "v")
+    for i in range(6):
+        p = 20 - 6 + i
+        a, b = lo[i], min(hi[i], p + 1)
+        assert np.all(np.abs(lse[i] - np.log(b - a)) < 1e-13)
+        for h in range(4):
+            assert np.max(np.abs(out[i, h] - V[a:b, h // 2].mean(axis=0))) < 1e-13
+
+
+def test_single_key_range_is_that_key(orc):
+    """Restricted to key j alone, O = V_j exactly and lse = s_j."""
+    w = synth.make_case(23, [5], [17], 4, 4, 2, 64)
+    V = dense_values(w, "v")
+    j = np.array([0, 4, 12, 7, 16], np.int32)
+    out, lse = run_oracle_lse(orc, w, key_lo=j, key_hi=j + 1)
+    for h in range(4):
+        s = brute_logits(w, 0, h)
+        for i in range(5):
+            assert np.array_equal(out[i, h], V[j[i], h // 2])
+            assert abs(lse[i, h] - s[i, j[i]]) < 1e-12
+
+
+def test_empty_range_is_zero_and_minus_inf(orc):
+    """A range beyond the row's causal bound (or empty) holds no key."""
+    w = synth.make_case(24, [4], [10], 4, 4, 2, 64)
+    lo = np.array([7, 7, 3, 5], np.int32)   # row i sees keys 0..6+i
+    hi = np.array([20, 20, 3, 5], np.int32)
+    out, lse = run_oracle_lse(orc, w, key_lo=lo, key_hi=hi)
+    assert np.all(lse[0] == -np.inf) and np.all(out[0] == 0.0)
+    assert np.all(lse[2] == -np.inf) and np.all(lse[3] == -np.inf)
+    assert np.all(np.isfinite(lse[1]))   # row 1 sees key 7 .. its bound 7
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_disjoint_ranges_merge_into_full_attention(orc, causal):
+    """Attention over disjoint key ranges merges into attention over their
+    union: O = sum_k exp(lse_k - lse) O_k, lse = log sum_k exp(lse_k), with
+    empty ranges (lse = -inf) weighing nothing."""
+    w = synth.make_case(25, [9, 5], [40, 23], 8, 4, 2, 64, causal=causal)
+    full, lse_full = run_oracle_lse(orc, w, causal=causal)
+    cuts = [0, 13, 31, 35, 1 << 20]
+    parts = [run_oracle_lse(orc, w, key_lo=a, key_hi=b, causal=causal) for a, b in zip(cuts, cuts[1:])]
+    lses = np.stack([p[1] for p in parts])
+    assert np.any(np.isneginf(lses))   # the causal case has rows that see no key of a range
+    m = np.max(lses, axis=0)
+    wts = np.exp(lses - m)
+    lse = m + np.log(wts.sum(axis=0))
+    o = sum(wt[..., None] * p[0] for wt, p in zip(wts, parts)) / wts.sum(axis=0)[..., None]
+    assert np.max(np.abs(lse - lse_full)) < 1e-12
+    assert np.max(np.abs(o - full)) < 1e-12
+
+
 # ------------------------------------------------------------------ placement
 def test_placement_invariance_with_poisoned_pool(orc):
     """The same bytes at the bottom, the top and scattered in a NaN-poisoned
