@@ -143,6 +143,52 @@ int pa_prefill_int8kv(const pa_paged_args *args, const void *q, const int8_t *k_
                       hipStream_t stream);
 
 /*
+ * Split-KV variants with log-sum-exp output (vllm.cpp PR #3360, "What
+ * changed": the bf16 prefill runs on a split-KV flash kernel; HyperQwen PR
+ * #91: the spec-decode verify attention, a few query tokens against a long
+ * cached context, computes per-range partial results that a combine step
+ * merges).  Each 128-column tile's keys are cut into up to num_splits ranges
+ * of whole 64-key tiles, one workgroup each, so that a short chunk over a long
+ * context still fills the GPU; a second kernel merges the ranges in a fixed
+ * order (the result is deterministic and independent of the placement).
+ *
+ * Key ranges: with n the column tile's 64-key tiles and f the number of them
+ * that no column of the tile masks (every key at or before the tile's first
+ * query position), split s < min(num_splits, f) (at least 1 split) takes
+ * tiles [s * f / se, (s + 1) * f / se) with se = max(1, min(num_splits, f)),
+ * the last one running on to n; splits s >= se take no key.  Column tiles are
+ * 128 consecutive (chunk row, q head of the KV head's group) pairs, rows
+ * major, of one (request, KV head).
+ *
+ *   num_splits  1 .. PA_MAX_SPLITS
+ *   o_part      fp32 [sum Lq, Hq, num_splits, D]: split s's attention over its
+ *               range, normalised by its own row sum (written for s < se)
+ *   lse_part    fp32 [sum Lq, Hq, num_splits]: log(sum_j exp(scale <q, K_j>))
+ *               over the range, natural log; -inf for a split with no key
+ *   out         [sum Lq, Hq, D] of out_dtype: sum_s e^{lse_s - lse} O_s
+ *   lse         fp32 [sum Lq, Hq] or NULL: log sum_s e^{lse_s}, the whole
+ *               row's log-sum-exp
+ * The workspace is the one of the non-split entry (pa_workspace_bytes with
+ * PA_ENTRY_PREFILL_BF16 / PA_ENTRY_PREFILL_INT8KV), and PA_FLAG_IMAGES_READY
+ * works as there.  Errors as the non-split entry, plus PA_ERR_SHAPE for
+ * num_splits out of range or a misaligned o_part (16 bytes), PA_ERR_NULL for
+ * a NULL o_part / lse_part, PA_ERR_TOO_LARGE for more than 65,535 requests or
+ * 2^31 workgroups (requests x Hkv x column tiles x num_splits).
+ */
+#define PA_MAX_SPLITS 256
+
+int pa_prefill_bf16_splitkv(const pa_paged_args *args, const void *q, const void *k_pool,
+                            const void *v_pool, int32_t num_splits, float *o_part,
+                            float *lse_part, void *out, int32_t out_dtype, float *lse,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+int pa_prefill_int8kv_splitkv(const pa_paged_args *args, const void *q, const int8_t *k_pool,
+                              const int8_t *v_pool, const float *k_scales,
+                              const float *v_scales, int32_t num_splits, float *o_part,
+                              float *lse_part, void *out, int32_t out_dtype, float *lse,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pa_k_stats -- first pass of the int8-QK prefill (HyperQwen PR #109: the
  * K-stats kernel reads K through the block table).  For every context token
  * t < L_r and KV head g:   ks[cu_ctx[r] + t, g] = max_d |K| / 127  (fp32).

@@ -71,6 +71,7 @@ AttnParams attn_params(const pa_paged_args *a) {
     p.scale = a->softmax_scale;
     p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
     p.causal = a->causal;
+    p.splits = 1;
     return p;
 }
 
@@ -165,16 +166,63 @@ ImageParams image_params(const pa_paged_args *a, void *ws, int kind) {
     return p;
 }
 
-}  // namespace
+// split-KV outputs of the *_splitkv entry points
+struct SplitOut {
+    int32_t n;          // key splits per column tile
+    float *o_part;      // [sum Lq, Hq, n, D]
+    float *lse_part;    // [sum Lq, Hq, n]
+    float *lse;         // [sum Lq, Hq] or null
+};
 
-extern "C" {
+int check_split(const pa_paged_args *a, const SplitOut &so) {
+    if (so.n < 1 || so.n > PA_MAX_SPLITS) return PA_ERR_SHAPE;
+    if (!so.o_part || !so.lse_part) return PA_ERR_NULL;
+    if (!aligned16(so.o_part)) return PA_ERR_SHAPE;
+    const int64_t items = (int64_t)a->num_reqs * a->num_kv_heads *
+                          attn_col_tiles(a->max_q_len, a->num_q_heads / a->num_kv_heads) * so.n;
+    if (items >= ((int64_t)1 << 31) || a->num_reqs > 65535) return PA_ERR_TOO_LARGE;
+    return PA_OK;
+}
 
-int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
-                    void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+// attention (split-KV partials when so is given) and, for split-KV, the merge
+int run_attention(const pa_paged_args *a, int kind, AttnParams &p, const SplitOut *so, void *out,
+                  int32_t out_dtype, hipStream_t stream) {
+    const bool out_bf16 = out_dtype == PA_DTYPE_BF16;
+    if (!so) {
+        p.out = out;
+        return launched(launch_attention(kind, a->head_dim, out_bf16, p, a->max_q_len, stream));
+    }
+    p.sched = nullptr;   // split-KV items run in their plain XCD-contiguous order
+    p.splits = so->n;
+    p.o_part = so->o_part;
+    p.lse_part = so->lse_part;
+    p.out = nullptr;
+    int rc = launched(launch_attention(kind, a->head_dim, false, p, a->max_q_len, stream));
+    if (rc) return rc;
+    MergeParams m{};
+    m.cu_q = a->cu_q_lens;
+    m.ctx_lens = a->ctx_lens;
+    m.stride_bt = a->stride_bt;
+    m.num_reqs = a->num_reqs;
+    m.Hq = a->num_q_heads;
+    m.D = a->head_dim;
+    m.block_size = a->block_size;
+    m.max_ctx = a->max_ctx_len;
+    m.splits = so->n;
+    m.o_part = so->o_part;
+    m.lse_part = so->lse_part;
+    m.out = out;
+    m.lse = so->lse;
+    return launched(launch_merge(m, out_bf16, a->max_q_len, stream));
+}
+
+int prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
+                 const SplitOut *so, void *out, int32_t out_dtype, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
     int rc = check_common(a, 2, true);
     if (rc) return rc;
     if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (so && (rc = check_split(a, *so))) return rc;
     if (!k_pool || !v_pool) return PA_ERR_NULL;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
     if ((rc = check_workspace(a, PA_ENTRY_PREFILL_BF16, workspace, workspace_bytes))) return rc;
@@ -183,24 +231,23 @@ int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, c
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, false, false, stream)))) return rc;
     AttnParams p = attn_params(a);
-    p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_BF16, workspace);
+    p.sched = so ? nullptr : schedule_ptr(a, PA_ENTRY_PREFILL_BF16, workspace);
     if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.q = q;
     p.k = k_pool;
     p.v_img = (const char *)workspace;
     p.img_tiles = ip.tiles;
-    p.out = out;
-    return launched(launch_attention(KIND_BF16, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
-                                     a->max_q_len, stream));
+    return run_attention(a, KIND_BF16, p, so, out, out_dtype, stream);
 }
 
-int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
-                      const int8_t *v_pool, const float *k_scales, const float *v_scales,
-                      void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+int prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
+                   const int8_t *v_pool, const float *k_scales, const float *v_scales,
+                   const SplitOut *so, void *out, int32_t out_dtype, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
     int rc = check_common(a, 1, true);
     if (rc) return rc;
     if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (so && (rc = check_split(a, *so))) return rc;
     if (!k_pool || !v_pool) return PA_ERR_NULL;
     if ((rc = check_scales(a, k_scales)) || (rc = check_scales(a, v_scales))) return rc;
     if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
@@ -213,15 +260,49 @@ int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_poo
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
     if (build && (rc = launched(launch_images(ip, true, true, stream)))) return rc;
     AttnParams p = attn_params(a);
-    p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_INT8KV, workspace);
+    p.sched = so ? nullptr : schedule_ptr(a, PA_ENTRY_PREFILL_INT8KV, workspace);
     if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
     p.q = q;
     p.v_img = (const char *)ip.dst;
     p.k_img = (const char *)ip.dst2;
     p.img_tiles = ip.tiles;
-    p.out = out;
-    return launched(launch_attention(KIND_I8KV, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
-                                     a->max_q_len, stream));
+    return run_attention(a, KIND_I8KV, p, so, out, out_dtype, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
+                    void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    return prefill_bf16(a, q, k_pool, v_pool, nullptr, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
+                      const int8_t *v_pool, const float *k_scales, const float *v_scales,
+                      void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    return prefill_int8kv(a, q, k_pool, v_pool, k_scales, v_scales, nullptr, out, out_dtype, workspace,
+                          workspace_bytes, stream);
+}
+
+int pa_prefill_bf16_splitkv(const pa_paged_args *a, const void *q, const void *k_pool,
+                            const void *v_pool, int32_t num_splits, float *o_part, float *lse_part,
+                            void *out, int32_t out_dtype, float *lse, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    const SplitOut so{num_splits, o_part, lse_part, lse};
+    return prefill_bf16(a, q, k_pool, v_pool, &so, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_prefill_int8kv_splitkv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
+                              const int8_t *v_pool, const float *k_scales, const float *v_scales,
+                              int32_t num_splits, float *o_part, float *lse_part, void *out,
+                              int32_t out_dtype, float *lse, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    const SplitOut so{num_splits, o_part, lse_part, lse};
+    return prefill_int8kv(a, q, k_pool, v_pool, k_scales, v_scales, &so, out, out_dtype, workspace,
+                          workspace_bytes, stream);
 }
 
 int pa_k_stats(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,

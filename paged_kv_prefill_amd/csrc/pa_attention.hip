@@ -182,14 +182,16 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     const int lane = tid & 63, wave = tid >> 6;
     const int lc = lane & 31, hf = lane >> 5;
 
-    // ---- work item: (request, KV head, column tile), from the schedule (a
-    // single request: XCD-contiguous item ranges, which is what the schedule
-    // would be)
+    // ---- work item: ((request * Hkv + KV head) * splits + key split) * tiles
+    // + column tile, from the schedule (a single request, or split-KV:
+    // XCD-contiguous item ranges)
     const int32_t item = P.sched ? P.sched[blockIdx.x] : (int32_t)xcd_remap(blockIdx.x, gridDim.x);
     if (item < 0) return;
     const uint32_t logical = (uint32_t)item;
     const int tile = (int)(logical % (uint32_t)P.tiles);
-    const int rest = (int)(logical / (uint32_t)P.tiles);
+    const uint32_t rest0 = logical / (uint32_t)P.tiles;
+    const int split = (int)(rest0 % (uint32_t)P.splits);
+    const int rest = (int)(rest0 / (uint32_t)P.splits);
     const int g = rest % P.Hkv;
     const int r = rest / P.Hkv;
     if (r >= P.num_reqs) return;
@@ -208,6 +210,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     const int pos_min = P.causal ? pos0 + c0 / group : L - 1;
     const int n_keys = pos_max + 1;
     const int n_tiles = (n_keys + BN - 1) / BN;
+    const int t_mask = (pos_min + 1) / BN;   // first tile that needs masking
+    // the key tiles this workgroup streams: all, or its split's range
+    int kt_begin = 0, kt_end = n_tiles;
+    if (P.o_part) split_tiles(split, P.splits, t_mask, n_tiles, kt_begin, kt_end);
 
     // ---- this lane's query column
     const int col = c0 + wave * 32 + lc;
@@ -217,6 +223,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     const int h = g * group + (ccol % group);
     const int my_pos = P.causal ? pos0 + tok : L - 1;
     const __bf16 *qrow = (const __bf16 *)P.q + ((int64_t)(q0 + tok) * P.Hq + h) * D;
+    const int64_t prow = ((int64_t)(q0 + tok) * P.Hq + h) * P.splits + split;   // split-KV partial row
+    if (kt_begin == kt_end) {   // a split with no keys: zero weight in the merge
+        if (col_valid && hf == 0) P.lse_part[prow] = -INFINITY;
+        return;
+    }
 
     // ---- Q operand (B of S^T = K Q^T), resident for the whole KV loop
     bf16x8 qf[C::QK8 ? 1 : C::KSTEPS];
@@ -529,17 +540,17 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // run, so the softmax's vector work overlaps matrix-core work.  K runs one
     // tile ahead of V: during step kt the LDS holds K(kt+1) and V(kt) and the
     // copies of K(kt+2) and V(kt+1) stream into the other stages.
-    const int t_mask = (pos_min + 1) / BN;   // first tile that needs masking
+    // Tiles are numbered absolutely; stage parity counts from kt_begin.
     f32x16 sa[2], sb[2];
-    dma_k(0, 0);
-    dma_v(0, 0);
-    dma_k(min(1, n_tiles - 1), 1);
+    dma_k(kt_begin, 0);
+    dma_v(kt_begin, 0);
+    dma_k(min(kt_begin + 1, kt_end - 1), 1);
     __syncthreads();
     qk_tile(0, sa);
-    if (t_mask == 0) mask_tile(sa, 0);
+    if (kt_begin >= t_mask) mask_tile(sa, kt_begin);
     float mx = tile_max(sa);
-    __syncthreads();   // every wave is done with K(0) before K(2) overwrites it
-    dma_k(min(2, n_tiles - 1), 0);
+    __syncthreads();   // every wave is done with K(first) before K(first + 2) overwrites it
+    dma_k(min(kt_begin + 2, kt_end - 1), 0);
 
     // ---- one pipelined step as a fixed sequence of slots.  Phase A: the QK
     // MFMAs of tile kt+1, each slot carrying one LDS operand read for a later
@@ -584,7 +595,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         // K(kt+1), done once every wave is past phase A), spread evenly over the
         // slots.  A tile index past the end re-copies the last tile into a stage
         // nobody reads again, which keeps the slots branch-free.
-        const int tk = min(kt + 3, n_tiles - 1), tv = min(kt + 1, n_tiles - 1);
+        const int tk = min(kt + 3, kt_end - 1), tv = min(kt + 1, kt_end - 1);
         const int kid_raw = k_src_id(tk);
         KSrc ksrc;
         const auto vsrc = v_src(tv);
@@ -722,10 +733,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     using no = std::false_type;
     u32x4 ka0[PFQ], ka1[PFQ];
 #pragma unroll
-    for (int m = 0; m < PFQ; ++m) ka0[m] = rdK(kstage(1) + k_rd, m);   // K(1), landed
+    for (int m = 0; m < PFQ; ++m) ka0[m] = rdK(kstage(1) + k_rd, m);   // K(first + 1), landed
     // steps whose next tile is unmasked, two at a time (stages 0 then 1)
-    const int end1 = min(t_mask, n_tiles) - 1;
-    int kt = 0;
+    const int end1 = min(t_mask, kt_end) - 1;
+    int kt = kt_begin;
     for (; kt + 1 < end1; kt += 2) {
         step(kt, 0, sa, sb, ka0, ka1, yes{}, no{});
         step(kt + 1, 1, sb, sa, ka1, ka0, yes{}, no{});
@@ -737,25 +748,32 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         for (int m = 0; m < PFQ; ++m) ka0[m] = ka1[m];
     };
     if (kt < end1) {
-        step(kt, kt & 1, sa, sb, ka0, ka1, yes{}, no{});
+        step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, yes{}, no{});
         ++kt;
         roll();
     }
     // steps whose next tile is masked (the last one or two)
-    for (; kt + 1 < n_tiles; ++kt) {
-        step(kt, kt & 1, sa, sb, ka0, ka1, yes{}, yes{});
+    for (; kt + 1 < kt_end; ++kt) {
+        step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, yes{}, yes{});
         roll();
     }
-    step(kt, kt & 1, sa, sb, ka0, ka1, no{}, no{});
+    step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, no{}, no{});
     // copies still in flight (the last steps re-copy into stages nobody reads)
     // land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
 
-    // ---- epilogue: O / l, row of this lane's column
+    // ---- epilogue: O / l, row of this lane's column; a split-KV partial also
+    // records its range's log-sum-exp, ln(sum_j e^{s_j}) = ln2 (m_run + log2 l)
     const float l_tot = sum_halves(l_run);
     const float inv = 1.0f / l_tot;
     if (!col_valid) return;
-    const int64_t orow = ((int64_t)(q0 + tok) * P.Hq + h) * D;
+    int64_t orow = ((int64_t)(q0 + tok) * P.Hq + h) * D;
+    float *out_f32 = (float *)P.out;
+    if (P.o_part) {
+        if (hf == 0) P.lse_part[prow] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+        out_f32 = P.o_part;
+        orow = prow * D;
+    }
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -767,7 +785,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
                 *(u32x2 *)((__bf16 *)P.out + orow + d) = w;
             } else {
-                *(f32x4 *)((float *)P.out + orow + d) = f32x4{v0, v1, v2, v3};
+                *(f32x4 *)(out_f32 + orow + d) = f32x4{v0, v1, v2, v3};
             }
         }
 }
@@ -958,11 +976,84 @@ hipError_t launch_schedule(const AttnParams &p, int32_t max_q_len, hipStream_t s
     return hipGetLastError();
 }
 
+// ---- split-KV merge (deterministic: the splits are summed in order).  One
+// wave per (chunk row, q head), D / 64 output elements per lane:
+//     m = max_s lse_s,  w_s = e^{lse_s - m} (0 for an empty split),
+//     O = sum_s w_s O_s / sum_s w_s,  lse = m + ln sum_s w_s.
+constexpr int MERGE_THREADS = 256;
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(const MergeParams P) {
+    constexpr int PER = D / 64;
+    const int r = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t pair = (int64_t)blockIdx.x * (MERGE_THREADS / 64) + wave;   // row * Hq + head
+    const int q0 = P.cu_q[r];
+    const int Lq = P.cu_q[r + 1] - q0;
+    const int L = P.ctx_lens[r];
+    // the attention skipped this request (its outputs stay untouched)
+    if (Lq <= 0 || Lq > L || L > P.max_ctx) return;
+    if ((int64_t)(L - 1) / P.block_size >= P.stride_bt) return;
+    if (pair >= (int64_t)Lq * P.Hq) return;
+    const int64_t ph = (int64_t)q0 * P.Hq + pair;
+    const float *ls = P.lse_part + ph * P.splits;
+    float m = -INFINITY;
+    for (int s = 0; s < P.splits; ++s) m = fmaxf(m, ls[s]);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float wsum = 0.f;
+    for (int s = 0; s < P.splits; ++s) {
+        const float l = ls[s];
+        if (l == -INFINITY) continue;
+        const float w = expf(l - m);
+        wsum += w;
+        const float *o = P.o_part + (ph * P.splits + s) * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += w * o[e];
+    }
+    const float inv = 1.0f / wsum;
+    if constexpr (OUT_BF16) {
+        __bf16 *dst = (__bf16 *)P.out + ph * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) dst[e] = (__bf16)(acc[e] * inv);
+    } else {
+        float *dst = (float *)P.out + ph * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) dst[e] = acc[e] * inv;
+    }
+    if (P.lse && lane == 0) P.lse[ph] = m + logf(wsum);
+}
+
+template <int D>
+static void launch_merge_d(const MergeParams &p, bool out_bf16, dim3 grid, hipStream_t s) {
+    if (out_bf16)
+        hipLaunchKernelGGL((merge_kernel<D, true>), grid, dim3(MERGE_THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((merge_kernel<D, false>), grid, dim3(MERGE_THREADS), 0, s, p);
+}
+
+hipError_t launch_merge(const MergeParams &p, bool out_bf16, int32_t max_q_len, hipStream_t stream) {
+    const int64_t pairs = (int64_t)max_q_len * p.Hq;
+    const int64_t gx = (pairs + MERGE_THREADS / 64 - 1) / (MERGE_THREADS / 64);
+    if (gx <= 0) return hipSuccess;
+    if (gx > 0x7fffffff || p.num_reqs > 65535 || p.splits < 1) return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)gx, (uint32_t)p.num_reqs);
+    switch (p.D) {
+        case 64: launch_merge_d<64>(p, out_bf16, grid, stream); break;
+        case 128: launch_merge_d<128>(p, out_bf16, grid, stream); break;
+        case 256: launch_merge_d<256>(p, out_bf16, grid, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,
                             int32_t max_q_len, hipStream_t stream) {
     AttnParams q = p;
     q.tiles = (int32_t)attn_col_tiles(max_q_len, p.group);
-    const int64_t nwg = attn_sched_slots(p.num_reqs, p.Hkv, max_q_len, p.group);
+    if (q.splits < 1 || (q.splits > 1 && !q.o_part)) return hipErrorInvalidValue;
+    const int64_t nwg = attn_sched_slots(p.num_reqs, p.Hkv, max_q_len, p.group, q.splits);
     if (nwg <= 0) return hipSuccess;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((uint32_t)nwg);

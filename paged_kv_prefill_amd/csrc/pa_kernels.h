@@ -35,6 +35,24 @@ struct AttnParams {
     const char *k_img;          // K tile images of an int8 pool (int8-KV exact arm)
     int64_t img_tiles;          // T: tiles per request in the image arrays
     void *out;
+    // split-KV: each column tile's keys are cut into `splits` ranges, one
+    // workgroup each; with o_part set every workgroup writes its range's
+    // normalised O and log-sum-exp there instead of out (see launch_merge)
+    int32_t splits;             // >= 1
+    float *o_part;              // [sum Lq, Hq, splits, D] fp32, or null
+    float *lse_part;            // [sum Lq, Hq, splits] fp32 (natural log)
+};
+
+// Merge of split-KV partials into the output (pa_merge in pa_attention.hip).
+struct MergeParams {
+    const int32_t *cu_q;
+    const int32_t *ctx_lens;
+    int64_t stride_bt;
+    int32_t num_reqs, Hq, D, block_size, max_ctx, splits;
+    const float *o_part;
+    const float *lse_part;
+    void *out;
+    float *lse;                 // [sum Lq, Hq] fp32 or null
 };
 
 enum AttnKind { KIND_BF16 = 0, KIND_I8KV = 1, KIND_QK8_VBF16 = 2, KIND_QK8_VI8 = 3 };
@@ -86,6 +104,8 @@ struct ImageParams {
 // launchers: return hipError_t of the launch
 hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,
                             int32_t max_q_len, hipStream_t stream);
+// O = sum_s exp(lse_s - lse) O_s, lse = log sum_s exp(lse_s), splits in order
+hipError_t launch_merge(const MergeParams &p, bool out_bf16, int32_t max_q_len, hipStream_t stream);
 // key rows per 1 KB K copy of an attention kind (fixes the tile's key order)
 int attn_rows_per_copy(int kind, int head_dim);
 hipError_t launch_images(const ImageParams &p, bool v_int8, bool k_image, hipStream_t stream);
@@ -107,9 +127,25 @@ inline int64_t attn_col_tiles(int32_t max_q_len, int32_t group) {
 }
 // entries of the work schedule, one per attention workgroup: the items,
 // rounded up to a whole number per XCD
-inline int64_t attn_sched_slots(int32_t num_reqs, int32_t num_kv_heads, int32_t max_q_len, int32_t group) {
-    const int64_t n = (int64_t)num_reqs * num_kv_heads * attn_col_tiles(max_q_len, group);
+inline int64_t attn_sched_slots(int32_t num_reqs, int32_t num_kv_heads, int32_t max_q_len, int32_t group,
+                                int32_t splits = 1) {
+    const int64_t n = (int64_t)num_reqs * num_kv_heads * attn_col_tiles(max_q_len, group) * splits;
     return (n + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+}
+// split-KV: the key tiles [begin, end) that split s of `splits` takes of a
+// column tile with n_tiles key tiles, the first t_full of which no column of
+// the tile masks.  The unmasked tiles are shared out evenly and the last split
+// also takes the masked ones, so every split that runs holds at least one
+// key of every column; splits beyond min(splits, t_full) (at least 1) get
+// nothing (begin == end).
+__host__ __device__ inline void split_tiles(int s, int splits, int t_full, int n_tiles, int &begin, int &end) {
+    const int se = t_full < 1 ? 1 : (splits < t_full ? splits : t_full);
+    if (s >= se) {
+        begin = end = 0;
+        return;
+    }
+    begin = (int)((int64_t)s * t_full / se);
+    end = s == se - 1 ? n_tiles : (int)((int64_t)(s + 1) * t_full / se);
 }
 
 }  // namespace pa

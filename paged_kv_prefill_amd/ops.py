@@ -23,7 +23,10 @@ PA_ENTRY_PREFILL_BF16, PA_ENTRY_PREFILL_INT8KV, PA_ENTRY_PREFILL_INT8QK = 1, 2, 
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_INT8, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 PA_FLAG_IMAGES_READY = 1
 
-ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_k_stats", "pa_k_quant",
+PA_MAX_SPLITS = 256
+
+ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
+                "pa_prefill_int8kv_splitkv", "pa_k_stats", "pa_k_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_gather_kv",
                 "pa_peak_probe", "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
 
@@ -62,6 +65,8 @@ def lib():
         sig = {
             "pa_prefill_bf16": [pa, vp, vp, vp, vp, i32, vp, sz, vp],
             "pa_prefill_int8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
+            "pa_prefill_bf16_splitkv": [pa, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
+            "pa_prefill_int8kv_splitkv": [pa, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
             "pa_k_stats": [pa, vp, i32, vp, vp, vp, vp],
             "pa_k_quant": [pa, vp, i32, vp, vp, vp, vp, vp],
             "pa_prefill_int8qk": [pa, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
@@ -192,6 +197,41 @@ def pa_prefill_int8kv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, out, ws=N
     _check(lib().pa_prefill_int8kv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(k_scales),
                                    _p(v_scales), _p(out), dt, wp, wn, _stream(stream)),
            "pa_prefill_int8kv")
+    return out
+
+
+def split_buffers(num_rows: int, num_q_heads: int, head_dim: int, num_splits: int, device):
+    """fp32 partial buffers of the split-KV entry points: O [rows, Hq, S, D]
+    and log-sum-exp [rows, Hq, S] (torch-owned)."""
+    o = torch.empty((num_rows, num_q_heads, num_splits, head_dim), dtype=torch.float32, device=device)
+    lse = torch.empty((num_rows, num_q_heads, num_splits), dtype=torch.float32, device=device)
+    return o, lse
+
+
+def pa_prefill_bf16_splitkv(p: Paged, q, k_pool, v_pool, out, num_splits, o_part=None,
+                            lse_part=None, lse=None, ws=None, stream=None):
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    if o_part is None or lse_part is None:
+        o_part, lse_part = split_buffers(q.shape[0], q.shape[1], q.shape[2], num_splits, q.device)
+    ws, wp, wn = _ws(p, PA_ENTRY_PREFILL_BF16, ws)
+    _check(lib().pa_prefill_bf16_splitkv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), int(num_splits),
+                                         _p(o_part), _p(lse_part), _p(out), dt, _p(lse), wp, wn,
+                                         _stream(stream)), "pa_prefill_bf16_splitkv")
+    return out
+
+
+def pa_prefill_int8kv_splitkv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, out, num_splits,
+                              o_part=None, lse_part=None, lse=None, ws=None, stream=None):
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    if o_part is None or lse_part is None:
+        o_part, lse_part = split_buffers(q.shape[0], q.shape[1], q.shape[2], num_splits, q.device)
+    ws, wp, wn = _ws(p, PA_ENTRY_PREFILL_INT8KV, ws)
+    _check(lib().pa_prefill_int8kv_splitkv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(k_scales),
+                                           _p(v_scales), int(num_splits), _p(o_part), _p(lse_part),
+                                           _p(out), dt, _p(lse), wp, wn, _stream(stream)),
+           "pa_prefill_int8kv_splitkv")
     return out
 
 

@@ -358,6 +358,36 @@ def config_batched(lite: bool = False) -> Workload:
                     BIG_D, bt, q, k, v)
 
 
+VERIFY_L = 60000
+VERIFY_Q = 8
+
+
+def config_verify(kv_format: str = "int8") -> Workload:
+    """Spec-decode verify: one request whose last 8 tokens (the drafted ones)
+    attend to a 60,000-token context; block 880, 4 KV / 16 q heads, head_dim
+    256, 2,600-block pool.  K/V bf16 (seed 6) or int8 with one fp32 scale per
+    token per KV head (seed 7).  Returned at the top placement (blocks
+    2,532..2,599); `bottom_block_table` holds blocks 0..68."""
+    rng = np.random.default_rng(6 if kv_format == "bf16" else 7)
+    ks = vs = None
+    if kv_format == "bf16":
+        k = normal_bf16(rng, (VERIFY_L, BIG_HKV, BIG_D))
+        v = normal_bf16(rng, (VERIFY_L, BIG_HKV, BIG_D))
+    elif kv_format == "int8":
+        k, ks = int8_per_token_head(rng, VERIFY_L, BIG_HKV, BIG_D)
+        v, vs = int8_per_token_head(rng, VERIFY_L, BIG_HKV, BIG_D)
+    else:
+        raise ValueError(kv_format)
+    q = normal_bf16(rng, (VERIFY_Q, BIG_HQ, BIG_D))
+    nb = -(-VERIFY_L // BIG_BS)                                      # 69 blocks
+    top = np.arange(BIGPOOL_BLOCKS - nb, BIGPOOL_BLOCKS, dtype=np.int32)[None, :]
+    w = Workload("verify_" + kv_format, kv_format, np.array([VERIFY_Q], np.int32),
+                 np.array([VERIFY_L], np.int32), BIG_BS, BIGPOOL_BLOCKS, BIG_HQ, BIG_HKV,
+                 BIG_D, top, q, k, v, ks, vs)
+    w.extra["bottom_block_table"] = np.arange(nb, dtype=np.int32)[None, :]
+    return w
+
+
 def chunk_rows(w: Workload, r: int) -> range:
     cu = w.cu_q_lens
     return range(int(cu[r]), int(cu[r + 1]))

@@ -108,6 +108,52 @@ def test_entry_point_specific_errors():
     assert L.pa_peak_probe(ops.PA_DTYPE_INT8, 1, 1 << 25, p, None) == ops.PA_ERR_SHAPE
 
 
+def test_split_kv_argument_errors():
+    """Every call fails validation (split count, partial buffers, sizes) before
+    anything is enqueued."""
+    L = ops.lib()
+    a = _args()
+    p = C.c_void_p(4096)
+    odd = C.c_void_p(4100)
+    big = 1 << 40
+    bf = L.pa_prefill_bf16_splitkv
+    i8 = L.pa_prefill_int8kv_splitkv
+    assert bf(C.byref(a), p, p, p, 0, p, p, p, 0, None, p, big, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(a), p, p, p, ops.PA_MAX_SPLITS + 1, p, p, p, 0, None, p, big, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(a), p, p, p, 4, None, p, p, 0, None, p, big, None) == ops.PA_ERR_NULL
+    assert bf(C.byref(a), p, p, p, 4, p, None, p, 0, None, p, big, None) == ops.PA_ERR_NULL
+    assert bf(C.byref(a), p, p, p, 4, odd, p, p, 0, None, p, big, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(a), p, p, p, 4, p, p, p, 5, None, p, big, None) == ops.PA_ERR_UNSUPPORTED
+    assert bf(None, p, p, p, 4, p, p, p, 0, None, p, big, None) == ops.PA_ERR_NULL
+    many = _args(num_reqs=70000)
+    assert bf(C.byref(many), p, p, p, 4, p, p, p, 0, None, p, big, None) == ops.PA_ERR_TOO_LARGE
+    assert i8(C.byref(a), p, p, p, p, p, 0, p, p, p, 0, None, p, big, None) == ops.PA_ERR_SHAPE
+    assert i8(C.byref(a), p, p, p, None, p, 4, p, p, p, 0, None, p, big, None) == ops.PA_ERR_NULL
+    assert i8(C.byref(a), p, p, p, p, p, 4, p, None, p, 0, None, p, big, None) == ops.PA_ERR_NULL
+
+
+def _split_tiles(s, splits, t_full, n_tiles):
+    """The documented key-range rule of the split-KV entry points."""
+    se = 1 if t_full < 1 else min(splits, t_full)
+    if s >= se:
+        return 0, 0
+    return s * t_full // se, (n_tiles if s == se - 1 else (s + 1) * t_full // se)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])
+@pytest.mark.parametrize("t_full,n_tiles", [(0, 1), (0, 2), (1, 2), (5, 6), (37, 39), (312, 313), (8, 8)])
+def test_split_ranges_cover_every_tile_once(splits, t_full, n_tiles):
+    """The ranges partition [0, n_tiles) in order, every non-empty range holds
+    an unmasked tile or starts at tile 0 (so each of its columns sees a key),
+    and no more than min(splits, max(t_full, 1)) are non-empty."""
+    got = [_split_tiles(s, splits, t_full, n_tiles) for s in range(splits)]
+    live = [(b, e) for b, e in got if e > b]
+    assert live[0][0] == 0 and live[-1][1] == n_tiles
+    assert all(x[1] == y[0] for x, y in zip(live, live[1:]))
+    assert len(live) == min(splits, max(t_full, 1))
+    assert all(b < t_full or b == 0 for b, e in live)
+
+
 def test_workspace_size_formula():
     """num_reqs * ceil(max_ctx / 64) * Hkv V^T images of 144 * D + 256 bytes
     (fp16 rows of 64 keys padded to 72), plus as many K images of 128 * D + 256
