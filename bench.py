@@ -19,7 +19,8 @@ throughput the chip sustains on the same instruction shape with no other work
 skipped via PA_FLAG_IMAGES_READY), its HBM bytes per launch from the committed
 counter profile when that was taken on this build, the CPU oracle's rate on a
 bounded sample, and the other arms (int8 KV exact-QK, int8-QK with its two K
-passes, fp8 KV through the dense bf16 scratch, the batched 8-request chunk)
+passes, fp8 KV through the dense bf16 scratch, the batched 8-request chunk,
+split-KV on a short chunk and on a spec-decode verify at 60,000 context)
 measured per call.
 """
 from __future__ import annotations
@@ -318,6 +319,72 @@ def arm_batched(steps, warmup):
                                "mfma_frac": fl / ms * 1e-9 / PEAK_BF16_TFLOPS}}
 
 
+def arm_splitkv(steps, warmup):
+    """Split-KV: (1) a short chunk (the bf16 workload's last 256 rows, 20,000
+    context) whose 32 column tiles alone would leave most CUs idle, plain
+    entry against 8 key splits; (2) spec-decode verify, 8 drafted tokens at a
+    60,000-token context (int8 per-token-head and bf16 KV) with 32 splits,
+    whole calls (V image pass + attention + merge) and attention + merge
+    alone (images reused)."""
+    res = {}
+    w = synth.config_bigpool_bf16()
+    lq = 256
+    ws_ = synth.Workload(**{**w.__dict__})
+    ws_.q_lens = np.array([lq], np.int32)
+    ws_.q = w.q[-lq:]
+    P = Pools(ws_, w.extra["top_block_table"])
+    p = P.paged()
+    out = P.out()
+    ws = ops.workspace(p, ops.PA_ENTRY_PREFILL_BF16)
+    ops.pa_prefill_bf16(p, P.q, P.k, P.v, out, ws)
+    pr = P.paged()
+    pr.flags = ops.PA_FLAG_IMAGES_READY
+    S = 8
+    o_part, lse_part = ops.split_buffers(lq, w.num_q_heads, w.head_dim, S, DEV)
+    fl = attn_flops(ws_)
+    (t_plain, t_split), _ = time_launches(
+        [lambda: ops.pa_prefill_bf16(pr, P.q, P.k, P.v, out, ws),
+         lambda: ops.pa_prefill_bf16_splitkv(pr, P.q, P.k, P.v, out, S, o_part, lse_part, None, ws)],
+        steps, warmup)
+    res["splitkv_chunk256_20k"] = {
+        "splits": S, "ms_plain": t_plain, "ms_split": t_split,
+        "tflops_plain": fl / t_plain * 1e-9, "tflops_split": fl / t_split * 1e-9,
+        "mfma_frac_split": fl / t_split * 1e-9 / PEAK_BF16_TFLOPS,
+        "note": "attention (+ merge) with the V images reused"}
+    del P, ws, o_part, lse_part
+    torch.cuda.empty_cache()
+    for fmt in ("int8", "bf16"):
+        w = synth.config_verify(fmt)
+        P = Pools(w, w.block_table)
+        p = P.paged()
+        out = P.out()
+        entry = ops.PA_ENTRY_PREFILL_BF16 if fmt == "bf16" else ops.PA_ENTRY_PREFILL_INT8KV
+        ws = ops.workspace(p, entry)
+        pr = P.paged()
+        pr.flags = ops.PA_FLAG_IMAGES_READY
+        S = 32
+        o_part, lse_part = ops.split_buffers(int(w.q_lens.sum()), w.num_q_heads, w.head_dim, S, DEV)
+        if fmt == "bf16":
+            f = lambda pp: ops.pa_prefill_bf16_splitkv(pp, P.q, P.k, P.v, out, S, o_part, lse_part,
+                                                       None, ws)
+        else:
+            f = lambda pp: ops.pa_prefill_int8kv_splitkv(pp, P.q, P.k, P.v, P.k_scales, P.v_scales,
+                                                         out, S, o_part, lse_part, None, ws)
+        (t_call,), _ = time_launches([lambda: f(p)], steps, warmup)
+        (t_ready,), _ = time_launches([lambda: f(pr)], steps, warmup)
+        L, hkv, d = int(w.ctx_lens[0]), w.num_kv_heads, w.head_dim
+        # algorithmic bytes: every K and V element (and int8 scale) of the context read once
+        kv_bytes = 2 * L * hkv * d * (1 if fmt == "int8" else 2) + (2 * L * hkv * 4 if fmt == "int8" else 0)
+        res[f"verify_60k_{fmt}"] = {
+            "splits": S, "ms_call": t_call, "ms_images_ready": t_ready,
+            "kv_bytes": kv_bytes, "gbs_call": kv_bytes / t_call * 1e-6,
+            "gbs_images_ready": kv_bytes / t_ready * 1e-6,
+            "hbm_frac_images_ready": kv_bytes / t_ready * 1e-6 / PEAK_HBM_GBS}
+        del P, ws, o_part, lse_part
+        torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -384,6 +451,9 @@ def main():
         torch.cuda.empty_cache()
         arms.update(arm_batched(args.steps, args.warmup))
         progress("batched arm")
+        torch.cuda.empty_cache()
+        arms.update(arm_splitkv(args.steps, args.warmup))
+        progress("split-KV arms")
         line["arms"] = arms
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, top)

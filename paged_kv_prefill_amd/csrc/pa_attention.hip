@@ -84,6 +84,9 @@ constexpr int QK_AHEAD = PA_QK_AHEAD;
 constexpr int PV_IN_A = PA_PV_IN_A;      // PV MFMAs in phase A per 24 of its PV-capable slots
 constexpr int PV_AHEAD = PA_PV_AHEAD;
 #define PA_FENCE() __builtin_amdgcn_sched_barrier(0)
+// every helper lambda of the kernel is inlined: an outlined one takes the
+// address of the kernel's by-value parameter block, which then lives in scratch
+#define PA_INL __attribute__((always_inline))
 static_assert(NTHR == ATTN_THREADS && NCOL == ATTN_COLS, "launch geometry");
 
 template <int D, int KIND>
@@ -291,8 +294,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 
     const int64_t img_base = ((int64_t)r * P.img_tiles) * P.Hkv + g;   // image index of tile 0
     const int64_t k8_row0 = C::QK8 ? (int64_t)P.cu_ctx[r] : 0;
-    auto kstage = [&](int s) { return smem + s * C::KSTAGE; };
-    auto vstage = [&](int s) { return smem + 2 * C::KSTAGE + s * C::VSTAGE; };
+    auto kstage = [&](int s) PA_INL { return smem + s * C::KSTAGE; };
+    auto vstage = [&](int s) PA_INL { return smem + 2 * C::KSTAGE + s * C::VSTAGE; };
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     // ---- per-lane constants of the K copies: lane l moves chunk l % KCPR of
@@ -319,8 +322,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     };
     // the block id behind a wave's copies of tile kt: an LDS read issued early
     // (k_src_id) and consumed later (k_src), so its latency hides behind MFMAs
-    auto k_src_key = [&](int kt) { return min(kt * BN + wave_u * 16, (n_keys - 1) & ~15); };
-    auto k_src_id = [&](int kt) -> int {
+    auto k_src_key = [&](int kt) PA_INL { return min(kt * BN + wave_u * 16, (n_keys - 1) & ~15); };
+    auto k_src_id = [&](int kt) PA_INL -> int {
         if constexpr (C::K_PAGED && FAST) {
             FastDiv fd{P.bsdiv.mul, P.bsdiv.shift, P.bsdiv.d};
             return bt_lds[(int)fdiv((uint32_t)k_src_key(kt), fd)];
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             return 0;
         }
     };
-    auto k_src = [&](int kt, int raw_id) -> KSrc {
+    auto k_src = [&](int kt, int raw_id) PA_INL -> KSrc {
         if constexpr (C::K_PAGED && FAST) {
             // a wave's copies cover 16 consecutive keys, so one cache block; a
             // wave whose keys are all past the context re-reads the last 16
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             return KSrc{rsrc_at(P.k), 0u};   // per-lane addresses below
         }
     };
-    auto k_copy = [&](const KSrc &src, int kt, int stage, int i) {
+    auto k_copy = [&](const KSrc &src, int kt, int stage, int i) PA_INL {
         char *kl = kstage(stage);
         const int kbase = kt * BN;
         if (i == C::K_PER_WAVE) {   // per-key scales
@@ -394,21 +397,21 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         }
     };
     constexpr int NKC = C::K_PER_WAVE + (C::K_SCALED ? 1 : 0);   // K copy instructions per wave
-    auto dma_k = [&](int kt, int stage) {
+    auto dma_k = [&](int kt, int stage) PA_INL {
         const KSrc src = k_src(kt, k_src_id(kt));
 #pragma unroll
         for (int i = 0; i < NKC; ++i) k_copy(src, kt, stage, i);
     };
 
     // ---- V^T tile kt (an image built by the V pass) into LDS stage `stage`
-    auto v_src = [&](int kt) { return rsrc_at(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D)); };
-    auto v_copy = [&](__amdgpu_buffer_rsrc_t img, int stage, int i) {
+    auto v_src = [&](int kt) PA_INL { return rsrc_at(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D)); };
+    auto v_copy = [&](__amdgpu_buffer_rsrc_t img, int stage, int i) PA_INL {
         char *vl = vstage(stage);
         const int q = i * NWAVE + wave_u;
         if (C::VCOPIES % NWAVE == 0 || q < C::VCOPIES) bdma16(img, lane * 16, q * 1024, vl + q * 1024);
     };
     constexpr int NVC = C::V_PER_WAVE;                           // V copy instructions per wave
-    auto dma_v = [&](int kt, int stage) {
+    auto dma_v = [&](int kt, int stage) PA_INL {
         const auto img = v_src(kt);
 #pragma unroll
         for (int i = 0; i < NVC; ++i) v_copy(img, stage, i);
@@ -421,10 +424,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // ---- S^T = K Q^T for the 2 blocks of 32 keys of a K stage (raw logits, the
     // int8-QK arm's times the key scale); A operands are read two
     // k-steps ahead of the MFMAs that use them
-    auto qk_tile = [&](int stage, f32x16 (&s)[2]) {
+    auto qk_tile = [&](int stage, f32x16 (&s)[2]) PA_INL {
         const char *kl = kstage(stage);
         const char *kr = kl + k_rd;
-        auto rd = [&](int ks, int kb) -> u32x4 { return *(const u32x4 *)(kr + kb * C::KB_STEP + ks * 32); };
+        auto rd = [&](int ks, int kb) PA_INL -> u32x4 { return *(const u32x4 *)(kr + kb * C::KB_STEP + ks * 32); };
         constexpr int PF = 2 < C::KSTEPS ? 2 : C::KSTEPS;
         u32x4 a[PF + 1][2];
 #pragma unroll
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 
     // causal / context mask of tile kt's logits (tiles that reach past the
     // workgroup's first column only)
-    auto mask_tile = [&](f32x16 (&s)[2], int kt) {
+    auto mask_tile = [&](f32x16 (&s)[2], int kt) PA_INL {
         const int lim = my_pos - kt * BN - hf * C::HSTEP;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) s[kb][i] = -INFINITY;
     };
     // column maximum of a tile's logits, log2 units
-    auto tile_max = [&](const f32x16 (&s)[2]) -> float {
+    auto tile_max = [&](const f32x16 (&s)[2]) PA_INL -> float {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -517,7 +520,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     };
     // lazy online-softmax update: move the reference maximum (and rescale O
     // and the row sum) only when some column's maximum grew past the slack
-    auto rescale = [&](float mx) {
+    auto rescale = [&](float mx) PA_INL {
         if (__any(mx > m_run + RESCALE_SLACK)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = exp2_fast(m_run - m_new);
@@ -570,10 +573,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // PV MFMAs spread over phase A's slots LAG.. (the rest go to phase B, where
     // they carry tile kt+1's post-processing)
     constexpr int NPA = (PV_IN_A * (NQ - LAG)) / 24 < NP ? (PV_IN_A * (NQ - LAG)) / 24 : NP;
-    auto rdK = [&](const char *kr, int m) -> u32x4 {
+    auto rdK = [&](const char *kr, int m) PA_INL -> u32x4 {
         return *(const u32x4 *)(kr + (m & 1) * C::KB_STEP + (m >> 1) * 32);
     };
-    auto rdV = [&](const char *vr, int n) -> f16x8 {   // V^T operand of PV MFMA n
+    auto rdV = [&](const char *vr, int n) PA_INL -> f16x8 {   // V^T operand of PV MFMA n
         return *(const f16x8 *)(vr + (n % C::DB) * 32 * VT_ROW_BYTES + (n / C::DB) * 32);
     };
 
@@ -581,7 +584,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // kin: the first PFQ K operands of tile kt+1, read by the previous step;
     // kout: the same for tile kt+2, read here in phase B
     auto step = [&](int kt, int cur, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&kin)[PFQ],
-                    u32x4 (&kout)[PFQ], auto has_next, auto mask_next) {
+                    u32x4 (&kout)[PFQ], auto has_next, auto mask_next) PA_INL {
         constexpr bool NEXT = decltype(has_next)::value;
         constexpr bool MASK = decltype(mask_next)::value;
         constexpr int N0 = NEXT ? NPA : 0;             // PV MFMAs issued in phase A
@@ -599,11 +602,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         const int kid_raw = k_src_id(tk);
         KSrc ksrc;
         const auto vsrc = v_src(tv);
-        auto copy_a = [&](int slot) {
+        auto copy_a = [&](int slot) PA_INL {
 #pragma unroll
             for (int c = slot * NVC / NQ; c < (slot + 1) * NVC / NQ; ++c) v_copy(vsrc, cur ^ 1, c);
         };
-        auto copy_b = [&](int slot) {
+        auto copy_b = [&](int slot) PA_INL {
 #pragma unroll
             for (int c = slot * NKC / NB; c < (slot + 1) * NKC / NB; ++c) k_copy(ksrc, tk, cur ^ 1, c);
         };
@@ -633,7 +636,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         // exponentials)
         float psum = 0.f;
         f16x8 pb[4];
-        auto exp_el = [&](int e) {
+        auto exp_el = [&](int e) PA_INL {
             const int kb = e >> 4, i = e & 15;
             const float p = exp2_fast(fmaf(sc[kb][i], smfac, -m_run));
             sc[kb][i] = p;
@@ -645,7 +648,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         };
         // PV MFMA n: O^T[dims of block n % DB] += V^T P^T over key step n / DB,
         // its V^T operand read PFV MFMAs ahead
-        auto pv = [&](int n) {
+        auto pv = [&](int n) PA_INL {
             if (n + PFV < NP) va[n + PFV] = rdV(vr, n + PFV);
             const int st = n / C::DB, db = n % C::DB;
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[n], pb[st], o[db], 0, 0, 0);
@@ -695,7 +698,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         // tile kt+1's logit for element e: scale, mask, running maximum
         float mxa = -INFINITY;
         const int lim = my_pos - (kt + 1) * BN - hf * C::HSTEP;
-        auto post_el = [&](int e) {
+        auto post_el = [&](int e) PA_INL {
             const int kb = e >> 4, i = e & 15;
             float v = C::QK8 ? (float)sacci[kb][i] : sacc[kb][i];
             if constexpr (C::K_SCALED) v *= ksc[kb][i >> 2][i & 3];   // per-key scale
@@ -741,7 +744,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         step(kt, 0, sa, sb, ka0, ka1, yes{}, no{});
         step(kt + 1, 1, sb, sa, ka1, ka0, yes{}, no{});
     }
-    auto roll = [&]() {
+    auto roll = [&]() PA_INL {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
 #pragma unroll
