@@ -64,6 +64,11 @@ def load(path: str | None = None):
     lib.oracle_fp8_dense_dequant.restype = i32
     lib.oracle_gather_kv.argtypes = paged + [i32p, i32p, i32] + geom + [i32, vp, vp]
     lib.oracle_gather_kv.restype = i32
+    lib.oracle_store_kv_int8.argtypes = paged + [i32p, i32p, i32] + geom + [u16p, u16p, i8p, i8p, f32p, f32p, i64, i64]
+    lib.oracle_store_kv_int8.restype = i32
+    lib.oracle_store_kv_fp8.argtypes = paged + [i32p, i32p, i32] + geom + [u16p, u16p, f32, f32, u8p, u8p]
+    lib.oracle_store_kv_fp8.restype = i32
+    lib.oracle_f32_to_e4m3fn_sat.argtypes = [f32p, u8p, i64]
     lib.oracle_bf16_from_f32.argtypes = [f32p, u16p, i64]
     lib.oracle_e4m3fn_to_f32.argtypes = [u8p, f32p, i64]
     lib.oracle_max_threads.restype = i32
@@ -243,6 +248,45 @@ def gather_kv(block_table, ctx_lens, pool, lib=None):
 
 
 # ------------------------------------------------------------------ codecs
+def store_kv_int8(block_table, ctx_lens, cu_new, k_new, v_new, k_pool, v_pool, k_scales, v_scales,
+                  lib=None):
+    """Quantise-on-store into host int8 pools (in place): request r's new rows
+    cu_new[r]..cu_new[r+1] go to the last positions of its context."""
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    nb, bs, hkv, d = k_pool.shape
+    sb, st, sh = _pool_strides(k_pool)
+    rc = lib.oracle_store_kv_int8(_ptr(bt), bt.shape[1], np.ascontiguousarray(ctx_lens, np.int32),
+                                  np.ascontiguousarray(cu_new, np.int32), len(ctx_lens), bs, hkv, d,
+                                  sb, st, sh, np.ascontiguousarray(k_new), np.ascontiguousarray(v_new),
+                                  k_pool, v_pool, k_scales, v_scales, bs * hkv, hkv)
+    if rc != 0:
+        raise ValueError(f"oracle_store_kv_int8 failed ({rc})")
+
+
+def store_kv_fp8(block_table, ctx_lens, cu_new, k_new, v_new, k_scale, v_scale, k_pool, v_pool,
+                 lib=None):
+    """Quantise-on-store into host fp8 e4m3fn pools (in place)."""
+    lib = lib or load()
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    nb, bs, hkv, d = k_pool.shape
+    sb, st, sh = _pool_strides(k_pool)
+    rc = lib.oracle_store_kv_fp8(_ptr(bt), bt.shape[1], np.ascontiguousarray(ctx_lens, np.int32),
+                                 np.ascontiguousarray(cu_new, np.int32), len(ctx_lens), bs, hkv, d,
+                                 sb, st, sh, np.ascontiguousarray(k_new), np.ascontiguousarray(v_new),
+                                 float(k_scale), float(v_scale), k_pool, v_pool)
+    if rc != 0:
+        raise ValueError(f"oracle_store_kv_fp8 failed ({rc})")
+
+
+def f32_to_e4m3fn_sat(x):
+    lib = load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    c = np.empty(x.shape, dtype=np.uint8)
+    lib.oracle_f32_to_e4m3fn_sat(x.reshape(-1), c.reshape(-1), x.size)
+    return c
+
+
 def bf16_from_f32(x):
     x = np.ascontiguousarray(x, dtype=np.float32)
     y = np.empty(x.shape, dtype=np.uint16)

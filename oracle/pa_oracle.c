@@ -46,6 +46,13 @@
  *    K, logits from the exact integer dot of the codes times sq * ks * scale,
  *    then softmax and PV in double precision.
  *
+ *  - Quantise-on-store writers: the new tokens of each request, written at
+ *    the end of its context through the block table, as int8 codes with a
+ *    per-token-head scale (HyperQwen PR #91, the int8_per_token_head cache;
+ *    the K-quant arithmetic) or as e4m3fn codes of x / scale with one scale
+ *    per tensor (vllm.cpp PR #3360, the fp8 cache), NaN kept, magnitudes
+ *    saturated at 448, nearest code with ties to the even mantissa.
+ *
  *  - fp8 dense dequant (vllm.cpp PR #3360, "What changed"): the fp8 cache is
  *    dequantised once into a dense bf16 scratch with one block per request of
  *    block_size = max_seq, so that an identity block table addresses it:
@@ -478,6 +485,120 @@ int oracle_fp8_dense_dequant(const int32_t *block_table, int64_t stride_bt,
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------ quantise on store */
+
+/* binary32 -> OCP e4m3fn by the format's definition: NaN gives S.1111.111;
+ * otherwise the magnitude saturates at the largest finite value (448) and
+ * takes the nearest of the finite codes 0x00..0x7e (which decode in
+ * increasing order), a tie going to the code with the even mantissa. */
+static uint8_t f32_to_e4m3fn_sat(float x) {
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x)) return (uint8_t)(sign | 0x7f);
+    double a = fabs((double)x);
+    if (a > 448.0) a = 448.0;
+    int lo = 0, hi = 0x7e;                 /* largest code whose value is <= a */
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if ((double)e4m3fn_to_f32((uint8_t)mid) <= a) lo = mid; else hi = mid - 1;
+    }
+    int c = lo;
+    if (c < 0x7e) {
+        double below = a - (double)e4m3fn_to_f32((uint8_t)c);
+        double above = (double)e4m3fn_to_f32((uint8_t)(c + 1)) - a;
+        if (above < below || (above == below && ((c + 1) & 1) == 0)) c = c + 1;
+    }
+    return (uint8_t)(sign | c);
+}
+
+/* Quantise-on-store into an int8 per-token-head pool (HyperQwen PR #91: the
+ * int8_per_token_head KV cache, its per-token-head scale indexed by the same
+ * block id as the codes).  Request r's n_r = cu_new[r+1] - cu_new[r] new
+ * tokens are the last n_r positions of its context: token j goes to position
+ * ctx_lens[r] - n_r + j.  Per (token, KV head), with x the bf16 value in fp32:
+ *     s = max_d |x| / 127,  code = clamp(round_half_even(x / s), -127, 127)
+ * (codes 0 when s == 0), the arithmetic of the K-quant pass.  new rows are
+ * [cu_new[num_reqs], num_kv_heads, head_dim] bf16 bits.  Returns -1 for a
+ * request with n_r < 0 or n_r > ctx_lens[r] (nothing of it written). */
+int oracle_store_kv_int8(const int32_t *block_table, int64_t stride_bt, const int32_t *ctx_lens,
+                         const int32_t *cu_new, int32_t num_reqs, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, int64_t stride_block,
+                         int64_t stride_tok, int64_t stride_head, const uint16_t *k_new,
+                         const uint16_t *v_new, int8_t *k_pool, int8_t *v_pool, float *k_scales,
+                         float *v_scales, int64_t stride_sblock, int64_t stride_stok) {
+    paged_view pv = {block_table, stride_bt, block_size, stride_block, stride_tok, stride_head};
+    int bad = 0;
+    for (int r = 0; r < num_reqs; ++r) {
+        int64_t n = (int64_t)cu_new[r + 1] - cu_new[r], L = ctx_lens[r];
+        if (n < 0 || n > L) { bad = 1; continue; }
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t pos = L - n + j;
+            for (int g = 0; g < num_kv_heads; ++g) {
+                int64_t src = (((int64_t)cu_new[r] + j) * num_kv_heads + g) * head_dim;
+                int64_t dst = paged_offset(&pv, r, pos, g);
+                int64_t sdst = scale_offset(&pv, stride_sblock, stride_stok, r, pos, g);
+                for (int which = 0; which < 2; ++which) {
+                    const uint16_t *x = (which ? v_new : k_new) + src;
+                    int8_t *codes = (which ? v_pool : k_pool) + dst;
+                    float amax = 0.0f;
+                    for (int d = 0; d < head_dim; ++d) {
+                        float a = fabsf(bf16_bits_to_f32(x[d]));
+                        if (a > amax) amax = a;
+                    }
+                    float s = amax / 127.0f;
+                    for (int d = 0; d < head_dim; ++d) {
+                        int8_t code = 0;
+                        if (s != 0.0f) {
+                            float y = nearbyintf(bf16_bits_to_f32(x[d]) / s);   /* ties to even */
+                            if (y > 127.0f) y = 127.0f;
+                            if (y < -127.0f) y = -127.0f;
+                            code = (int8_t)y;
+                        }
+                        codes[d] = code;
+                    }
+                    (which ? v_scales : k_scales)[sdst] = s;
+                }
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Quantise-on-store into an fp8 e4m3fn pool with one fp32 scale per tensor
+ * (vllm.cpp PR #3360: the fp8 KV cache that the dense dequant reads back):
+ * code = e4m3fn_sat(x / scale), fp32 division, placement as above. */
+int oracle_store_kv_fp8(const int32_t *block_table, int64_t stride_bt, const int32_t *ctx_lens,
+                        const int32_t *cu_new, int32_t num_reqs, int32_t block_size,
+                        int32_t num_kv_heads, int32_t head_dim, int64_t stride_block,
+                        int64_t stride_tok, int64_t stride_head, const uint16_t *k_new,
+                        const uint16_t *v_new, float k_scale, float v_scale, uint8_t *k_pool,
+                        uint8_t *v_pool) {
+    paged_view pv = {block_table, stride_bt, block_size, stride_block, stride_tok, stride_head};
+    int bad = 0;
+    for (int r = 0; r < num_reqs; ++r) {
+        int64_t n = (int64_t)cu_new[r + 1] - cu_new[r], L = ctx_lens[r];
+        if (n < 0 || n > L) { bad = 1; continue; }
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t pos = L - n + j;
+            for (int g = 0; g < num_kv_heads; ++g) {
+                int64_t src = (((int64_t)cu_new[r] + j) * num_kv_heads + g) * head_dim;
+                int64_t dst = paged_offset(&pv, r, pos, g);
+                for (int d = 0; d < head_dim; ++d) {
+                    k_pool[dst + d] = f32_to_e4m3fn_sat(bf16_bits_to_f32(k_new[src + d]) / k_scale);
+                    v_pool[dst + d] = f32_to_e4m3fn_sat(bf16_bits_to_f32(v_new[src + d]) / v_scale);
+                }
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Vector helper for the pins: e4m3fn_sat of each fp32 value. */
+void oracle_f32_to_e4m3fn_sat(const float *x, uint8_t *c, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) c[i] = f32_to_e4m3fn_sat(x[i]);
 }
 
 /* ------------------------------------------------------------ gather */

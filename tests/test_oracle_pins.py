@@ -433,6 +433,110 @@ def test_fp8_dense_dequant_matches_torch_casts(orc, pow2):
             assert np.array_equal(dec_bf16(got[0, :50]), dec.double().numpy() * float(scale))
 
 
+# ------------------------------------------------------------------ quantise on store
+def _all_e4m3fn_values():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    return codes, vals
+
+
+def test_e4m3fn_encode_matches_torch_below_saturation(orc):
+    """Below 464 (the midpoint past 448) torch's round-to-nearest-even cast
+    and the oracle's nearest-code search agree bit for bit, on random values,
+    on every code's own value and on every midpoint between neighbours (the
+    ties, which go to the even mantissa)."""
+    codes, vals = _all_e4m3fn_values()
+    fin = np.sort(vals[np.isfinite(vals) & (vals >= 0)]).astype(np.float64)
+    mids = (fin[:-1] + fin[1:]) / 2
+    rng = np.random.default_rng(31)
+    x = np.concatenate([fin, mids, rng.uniform(-463.9, 463.9, 20000),
+                        rng.standard_normal(20000) * 0.01, [460.0, 463.99, -455.0]]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    got = orc.f32_to_e4m3fn_sat(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3fn_encode_saturates_and_keeps_nan(orc):
+    x = np.array([464.0, 480.0, 1e30, np.inf, -464.0, -np.inf, np.nan, -np.nan], np.float32)
+    got = orc.f32_to_e4m3fn_sat(x)
+    assert got[:4].tolist() == [0x7E] * 4 and got[4:6].tolist() == [0xFE] * 2
+    assert (got[6] & 0x7F) == 0x7F and (got[7] & 0x7F) == 0x7F
+
+
+def test_e4m3fn_encode_round_trips_every_code(orc):
+    codes, vals = _all_e4m3fn_values()
+    fin = np.isfinite(vals)
+    got = orc.f32_to_e4m3fn_sat(vals[fin])
+    assert np.array_equal(got, codes[fin])
+
+
+def _store_case(seed, fmt):
+    """A bf16 workload whose chunk tokens are the ones stored: request r's new
+    rows are the K/V rows of its last q_lens[r] positions."""
+    w = synth.make_case(seed, [6, 1, 17], [40, 9, 17], 8, 4, 2, 64, num_blocks=16)
+    cu = w.cu_ctx_lens
+    rows = np.concatenate([np.arange(cu[r + 1] - w.q_lens[r], cu[r + 1]) for r in range(w.num_reqs)])
+    return w, w.k[rows], w.v[rows]
+
+
+def test_store_int8_equals_k_stats_and_k_quant(orc):
+    """Stored codes and scales at the new positions equal the K-stats and
+    K-quant passes' output for the same values (both pinned above); every
+    other slot keeps its previous bytes."""
+    w, k_new, v_new = _store_case(41, "int8")
+    shape = w.pool_shape
+    kp = np.full(shape, 55, np.int8)
+    vp = np.full(shape, 55, np.int8)
+    ksp = np.full(shape[:3], np.nan, np.float32)
+    vsp = np.full(shape[:3], np.nan, np.float32)
+    orc.store_kv_int8(w.block_table, w.ctx_lens, w.cu_q_lens, k_new, v_new, kp, vp, ksp, vsp)
+    bf = synth.host_pools(w)
+    cu = w.cu_ctx_lens
+    for which, pool, spool in (("k", kp, ksp), ("v", vp, vsp)):
+        ks = orc.k_stats(w.block_table, w.ctx_lens, bf[which])
+        k8 = orc.k_quant(w.block_table, w.ctx_lens, bf[which], ks)
+        codes = orc.gather_kv(w.block_table, w.ctx_lens, pool)
+        for r in range(w.num_reqs):
+            a, b = int(cu[r + 1] - w.q_lens[r]), int(cu[r + 1])
+            assert np.array_equal(codes[a:b], k8[a:b])
+            assert np.all(codes[cu[r]:a] == 55)
+            for t in range(int(w.ctx_lens[r])):
+                pos_blk = w.block_table[r, t // w.block_size]
+                got = spool[pos_blk, t % w.block_size]
+                if cu[r] + t >= a:
+                    assert np.array_equal(got, ks[cu[r] + t])
+                else:
+                    assert np.all(np.isnan(got))
+
+
+def test_store_fp8_recovers_codes_of_representable_values(orc):
+    """Values that are e4m3fn codes times the scale (rounded to bf16, a
+    relative error far below half the code spacing) store back as exactly
+    those codes, with and without a power-of-two scale."""
+    rng = np.random.default_rng(43)
+    for scale in (np.float32(0.015625), np.float32(0.0173)):
+        w, _, _ = _store_case(42, "fp8")
+        n = int(w.q_lens.sum())
+        codes = rng.integers(0, 256, size=(n, w.num_kv_heads, w.head_dim)).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x11            # finite codes only
+        dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float()
+        x = synth.f32_to_bf16_bits((dec * float(scale)).numpy())
+        kp = np.full(w.pool_shape, 0x7F, np.uint8)
+        vp = np.full(w.pool_shape, 0x7F, np.uint8)
+        orc.store_kv_fp8(w.block_table, w.ctx_lens, w.cu_q_lens, x, x, scale, scale, kp, vp)
+        got = orc.gather_kv(w.block_table, w.ctx_lens, kp)
+        cu = w.cu_ctx_lens
+        off = 0
+        for r in range(w.num_reqs):
+            a, b = int(cu[r + 1] - w.q_lens[r]), int(cu[r + 1])
+            exp = codes[off:off + b - a]                     # -0 (0x80) stays -0
+            assert np.array_equal(got[a:b], exp)
+            assert np.all(got[cu[r]:a] == 0x7F)
+            off += b - a
+        assert np.array_equal(orc.gather_kv(w.block_table, w.ctx_lens, vp), got)
+
+
 # ------------------------------------------------------------------ int8-QK arm
 def _quant_exact_rows(rng, shape, step):
     """bf16 rows n * step with integers |n| <= 127 and one |n| = 127 per row,
