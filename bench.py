@@ -20,8 +20,8 @@ skipped via PA_FLAG_IMAGES_READY), its HBM bytes per launch from the committed
 counter profile when that was taken on this build, the CPU oracle's rate on a
 bounded sample, and the other arms (int8 KV exact-QK, int8-QK with its two K
 passes, fp8 KV through the dense bf16 scratch, the batched 8-request chunk,
-split-KV on a short chunk and on a spec-decode verify at 60,000 context)
-measured per call.
+split-KV on a short chunk and on a spec-decode verify at 60,000 context, the
+quantise-on-store writers) measured per call.
 """
 from __future__ import annotations
 
@@ -385,6 +385,46 @@ def arm_splitkv(steps, warmup):
     return res
 
 
+def arm_store(steps, warmup):
+    """Quantise-on-store into int8 per-token-head and fp8 pools at the top of the
+    2,600-block pool: the 2,048-token chunk, and the whole 20,000-token prompt
+    (the call that fills a request's pool).  Algorithmic bytes: bf16 K and V
+    read, codes (and int8 scales) written."""
+    w = synth.config_bigpool_bf16()
+    top = w.extra["top_block_table"]
+    shape = w.pool_shape
+    hkv, d = w.num_kv_heads, w.head_dim
+    k8 = torch.zeros(shape, dtype=torch.int8, device=DEV)
+    v8 = torch.zeros(shape, dtype=torch.int8, device=DEV)
+    ks = torch.zeros(shape[:3], dtype=torch.float32, device=DEV)
+    vs = torch.zeros(shape[:3], dtype=torch.float32, device=DEV)
+    kf = torch.zeros(shape, dtype=torch.uint8, device=DEV)
+    vf = torch.zeros(shape, dtype=torch.uint8, device=DEV)
+    fsc = torch.tensor([0.0173], dtype=torch.float32, device=DEV)
+    bt = dev(top)
+    ctx = dev(w.ctx_lens)
+    L = int(w.ctx_lens[0])
+    k_all, v_all = dev_bf16(w.k), dev_bf16(w.v)
+    res = {}
+    for name, n in (("chunk_2048", synth.CHUNK), ("prompt_20k", L)):
+        cu = dev(np.array([0, n], np.int32))
+        p = ops.Paged(bt, cu, ctx, n, L, w.block_size, w.num_blocks, w.num_q_heads, hkv, d,
+                      w.softmax_scale, True)
+        kn, vn = k_all[L - n:], v_all[L - n:]
+        (t8, tf), _ = time_launches(
+            [lambda: ops.pa_store_kv_int8(p, kn, vn, k8, v8, ks, vs),
+             lambda: ops.pa_store_kv_fp8(p, kn, vn, fsc, fsc, kf, vf)], steps, warmup)
+        elems = 2 * n * hkv * d
+        b8 = elems * 2 + elems + 2 * n * hkv * 4
+        bf = elems * 2 + elems
+        res[f"store_{name}"] = {
+            "int8": {"ms": t8, "gbs": b8 / t8 * 1e-6, "hbm_frac": b8 / t8 * 1e-6 / PEAK_HBM_GBS},
+            "fp8": {"ms": tf, "gbs": bf / tf * 1e-6, "hbm_frac": bf / tf * 1e-6 / PEAK_HBM_GBS}}
+    del k8, v8, ks, vs, kf, vf
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -454,6 +494,8 @@ def main():
         torch.cuda.empty_cache()
         arms.update(arm_splitkv(args.steps, args.warmup))
         progress("split-KV arms")
+        arms.update(arm_store(args.steps, args.warmup))
+        progress("store arms")
         line["arms"] = arms
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, top)

@@ -257,6 +257,36 @@ int pa_fp8_dense_dequant(const pa_paged_args *args, const uint8_t *k_pool,
                          hipStream_t stream);
 
 /*
+ * pa_store_kv_int8 / pa_store_kv_fp8 -- quantise-on-store writers that fill a
+ * quantised pool as chunks arrive (HyperQwen PR #91: the int8_per_token_head
+ * KV cache, whose per-token-head scale shares the codes' block id; vllm.cpp
+ * PR #3360: the fp8 e4m3 KV cache with one scale per tensor).  The new tokens
+ * of request r are its chunk, rows cu_q_lens[r] .. cu_q_lens[r+1] of k_new /
+ * v_new (bf16 [sum Lq, Hkv, D], 16-byte aligned), and go to the LAST Lq_r
+ * positions of its context: row j to position ctx_lens[r] - Lq_r + j, through
+ * the block table.  max_q_len bounds Lq_r as for the attention.
+ *   int8: per (token, KV head) s = max_d |x| / 127 (fp32), code =
+ *         clamp(round_half_even(x / s), -127, 127), codes 0 when s == 0;
+ *         writes the codes to k_pool / v_pool and s to k_scales / v_scales
+ *         (fp32 [num_blocks, block_size, Hkv] via stride_sblock / stride_stok)
+ *         -- the K-quant pass's arithmetic, bit for bit.
+ *   fp8:  code = e4m3fn(x / scale) with the tensor's scale (device fp32
+ *         scalars k_scale / v_scale, > 0): fp32 division, NaN stored as 0x7f,
+ *         magnitudes saturated at 448, round to nearest with ties to even.
+ * Requests whose lengths are inconsistent (Lq > L, L beyond the table row or
+ * max_ctx_len) are skipped; rows whose block id lies outside the pool are not
+ * written.  Errors: PA_ERR_NULL for a NULL pointer, PA_ERR_SHAPE for
+ * misaligned rows or pools, plus the common checks.
+ */
+int pa_store_kv_int8(const pa_paged_args *args, const void *k_new, const void *v_new,
+                     int8_t *k_pool, int8_t *v_pool, float *k_scales, float *v_scales,
+                     hipStream_t stream);
+
+int pa_store_kv_fp8(const pa_paged_args *args, const void *k_new, const void *v_new,
+                    const float *k_scale, const float *v_scale, uint8_t *k_pool, uint8_t *v_pool,
+                    hipStream_t stream);
+
+/*
  * pa_gather_kv -- test export: copy a paged pool's rows to a dense buffer by
  * position, dense[cu_ctx[r] + t, g, :] = pool row (r, t, g), elem_bytes 1 or 2.
  * Exercises the same 64-bit block addressing as the attention kernels.

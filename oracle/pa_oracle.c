@@ -50,7 +50,7 @@
  *    the end of its context through the block table, as int8 codes with a
  *    per-token-head scale (HyperQwen PR #91, the int8_per_token_head cache;
  *    the K-quant arithmetic) or as e4m3fn codes of x / scale with one scale
- *    per tensor (vllm.cpp PR #3360, the fp8 cache), NaN kept, magnitudes
+ *    per tensor (vllm.cpp PR #3360, the fp8 cache), NaN as 0x7f, magnitudes
  *    saturated at 448, nearest code with ties to the even mantissa.
  *
  *  - fp8 dense dequant (vllm.cpp PR #3360, "What changed"): the fp8 cache is
@@ -489,13 +489,13 @@ int oracle_fp8_dense_dequant(const int32_t *block_table, int64_t stride_bt,
 
 /* ------------------------------------------------------------ quantise on store */
 
-/* binary32 -> OCP e4m3fn by the format's definition: NaN gives S.1111.111;
+/* binary32 -> OCP e4m3fn by the format's definition: NaN gives 0.1111.111;
  * otherwise the magnitude saturates at the largest finite value (448) and
  * takes the nearest of the finite codes 0x00..0x7e (which decode in
  * increasing order), a tie going to the code with the even mantissa. */
 static uint8_t f32_to_e4m3fn_sat(float x) {
     uint8_t sign = signbit(x) ? 0x80 : 0x00;
-    if (isnan(x)) return (uint8_t)(sign | 0x7f);
+    if (isnan(x)) return 0x7f;
     double a = fabs((double)x);
     if (a > 448.0) a = 448.0;
     int lo = 0, hi = 0x7e;                 /* largest code whose value is <= a */

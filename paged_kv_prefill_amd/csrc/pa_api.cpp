@@ -418,6 +418,46 @@ int pa_gather_kv(const pa_paged_args *a, const void *pool, int32_t elem_bytes,
     return launched(launch_gather(p, stream));
 }
 
+int pa_store_kv_int8(const pa_paged_args *a, const void *k_new, const void *v_new, int8_t *k_pool,
+                     int8_t *v_pool, float *k_scales, float *v_scales, hipStream_t stream) {
+    int rc = check_common(a, 1, true);
+    if (rc) return rc;
+    if (!k_new || !v_new || !k_pool || !v_pool) return PA_ERR_NULL;
+    if ((rc = check_scales(a, k_scales)) || (rc = check_scales(a, v_scales))) return rc;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_SHAPE;
+    PassParams p = pass_params(a);
+    p.cu_new = a->cu_q_lens;
+    p.max_new = a->max_q_len;
+    p.src = k_new;
+    p.src2 = v_new;
+    p.dst = k_pool;
+    p.dst2 = v_pool;
+    p.dst_scales = k_scales;
+    p.dst2_scales = v_scales;
+    return launched(launch_store_int8(p, stream));
+}
+
+int pa_store_kv_fp8(const pa_paged_args *a, const void *k_new, const void *v_new,
+                    const float *k_scale, const float *v_scale, uint8_t *k_pool, uint8_t *v_pool,
+                    hipStream_t stream) {
+    int rc = check_common(a, 1, true);
+    if (rc) return rc;
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale) return PA_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_SHAPE;
+    PassParams p = pass_params(a);
+    p.cu_new = a->cu_q_lens;
+    p.max_new = a->max_q_len;
+    p.src = k_new;
+    p.src2 = v_new;
+    p.fscale = k_scale;
+    p.fscale2 = v_scale;
+    p.dst = k_pool;
+    p.dst2 = v_pool;
+    return launched(launch_store_fp8(p, stream));
+}
+
 int pa_peak_probe(int32_t dtype, int32_t workgroups, int32_t iters, float *out, hipStream_t stream) {
     if (dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_INT8) return PA_ERR_UNSUPPORTED;
     if (!out) return PA_ERR_NULL;

@@ -79,6 +79,14 @@ struct PassParams {
     int32_t max_seq;            // fp8 scratch rows per request
     int32_t elem_bytes;         // gather
     int32_t src_int8;           // K passes: 1 int8 pool, 0 bf16 pool
+    // quantise-on-store: new K/V rows (src, src2: bf16 [sum n, Hkv, D]) of
+    // request r are cu_new[r] .. cu_new[r+1], stored at the last positions of
+    // its context into dst / dst2 (int8 or fp8 pools) and, for int8, their
+    // per-token-head scales into dst_scales / dst2_scales
+    const int32_t *cu_new;
+    float *dst_scales;
+    float *dst2_scales;
+    int32_t max_new;            // host bound on new tokens per request
 };
 
 // Tile-image passes (pa_images.hip).
@@ -115,6 +123,8 @@ hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);
 hipError_t launch_k_quant(const PassParams &p, hipStream_t stream);
 hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t stream);
 hipError_t launch_gather(const PassParams &p, hipStream_t stream);
+hipError_t launch_store_int8(const PassParams &p, hipStream_t stream);
+hipError_t launch_store_fp8(const PassParams &p, hipStream_t stream);
 hipError_t launch_probe(bool int8, int32_t workgroups, int32_t iters, float *out, hipStream_t stream);
 
 constexpr int ATTN_THREADS = 256;

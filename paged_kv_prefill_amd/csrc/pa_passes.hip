@@ -7,6 +7,11 @@
 //   fp8 dense dequant (vllm.cpp PR #3360, "What changed"):
 //            scratch[r, t, g, d] = bf16_rne(fp32(e4m3fn(code)) * scale)
 //   gather   (test export): dense[t, g, :] = pool row (t, g)
+//   quantise-on-store (HyperQwen PR #91: the int8_per_token_head KV cache;
+//            vllm.cpp PR #3360: the fp8 KV cache), new tokens written at the
+//            end of each request's context:
+//            int8: s = max_d |x| / 127, code = clamp(rne(x / s), -127, 127)
+//            fp8:  code = e4m3fn(x / scale), saturated at 448, ties to even
 //
 // Each (token, KV head) row is split into 16-byte chunks, one per lane; the
 // lanes of a row are consecutive, so a wave reads whole rows with coalesced
@@ -168,6 +173,108 @@ __global__ __launch_bounds__(PT) void gather_kernel(const PassParams P) {
     }
 }
 
+// ---- quantise-on-store.  One (new token, KV head) row of K and of V per
+// group of D / 8 lanes, 8 bf16 values per lane.
+__device__ __forceinline__ bool store_row(const PassParams &P, int r, int64_t row, int64_t &src,
+                                         int64_t &off, int64_t &soff) {
+    int L;
+    if (!request_ok(P, r, L)) return false;
+    const int n0 = P.cu_new[r], n = P.cu_new[r + 1] - n0;
+    if (n < 0 || n > L || row >= (int64_t)n * P.Hkv) return false;
+    const int j = (int)((uint32_t)row / (uint32_t)P.Hkv), g = (int)((uint32_t)row % (uint32_t)P.Hkv);
+    src = ((int64_t)n0 * P.Hkv + row) * P.D;
+    return pass_row(P, r, L - n + j, g, off, soff);
+}
+
+__device__ __forceinline__ void load8(const void *base, int64_t at, float *x) {
+    const u32x4 w = *(const u32x4 *)((const __bf16 *)base + at);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]);
+}
+
+__global__ __launch_bounds__(PT) void store_int8_kernel(const PassParams P) {
+    const int r = blockIdx.y;
+    const int lpr = P.D / 8;   // lanes per row (8, 16 or 32), consecutive within a wave
+    const int sub = threadIdx.x % lpr, rl = threadIdx.x / lpr, rpw = PT / lpr;
+    const int64_t nrows = (int64_t)P.max_new * P.Hkv;
+    // every lane runs the same trip count, so the row reductions below stay
+    // uniform within a row's lanes
+    for (int64_t row = (int64_t)blockIdx.x * rpw + rl; row < nrows; row += (int64_t)gridDim.x * rpw) {
+        int64_t src = 0, off = 0, soff = 0;
+        const bool ok = store_row(P, r, row, src, off, soff);
+        float k[8], v[8];
+        if (ok) {
+            load8(P.src, src + sub * 8, k);
+            load8(P.src2, src + sub * 8, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) k[e] = v[e] = 0.f;
+        }
+        float ka = 0.f, va = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ka = fmaxf(ka, fabsf(k[e]));
+            va = fmaxf(va, fabsf(v[e]));
+        }
+        for (int m = 1; m < lpr; m <<= 1) {
+            ka = fmaxf(ka, __shfl_xor(ka, m, 64));
+            va = fmaxf(va, __shfl_xor(va, m, 64));
+        }
+        if (!ok) continue;
+        const float ks = ka / 127.0f, vs = va / 127.0f;
+        *(u32x2 *)((int8_t *)P.dst + off + sub * 8) = u32x2{quant4(k, ks), quant4(k + 4, ks)};
+        *(u32x2 *)((int8_t *)P.dst2 + off + sub * 8) = u32x2{quant4(v, vs), quant4(v + 4, vs)};
+        if (sub == 0) {
+            P.dst_scales[soff] = ks;
+            P.dst2_scales[soff] = vs;
+        }
+    }
+}
+
+// binary32 -> e4m3fn: NaN -> 0x7f (whatever its sign: the sign of a NaN that
+// a division produced is not portable); magnitudes saturate at 448; below
+// 2^-6 the grid is 2^-9 (subnormals, rounded as an integer multiple); above,
+// the fp32 mantissa is rounded to 3 bits half-to-even and the exponent
+// rebiased from 127 to 7 (a carry out of the mantissa bumps the exponent).
+__device__ __forceinline__ uint32_t e4m3fn_sat(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t au = u & 0x7fffffffu;
+    if (au > 0x7f800000u) return 0x7fu;
+    const float a = fminf(__uint_as_float(au), 448.0f);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)rintf(a * 512.0f);
+    } else {
+        uint32_t b = __float_as_uint(a);
+        b += 0x7ffffu + ((b >> 20) & 1u);
+        code = ((((b >> 23) & 0xffu) - 120u) << 3) | ((b >> 20) & 7u);
+    }
+    return sign | code;
+}
+
+__device__ __forceinline__ uint32_t fp8x4(const float *x, float scale) {
+    return e4m3fn_sat(x[0] / scale) | (e4m3fn_sat(x[1] / scale) << 8) | (e4m3fn_sat(x[2] / scale) << 16) |
+           (e4m3fn_sat(x[3] / scale) << 24);
+}
+
+__global__ __launch_bounds__(PT) void store_fp8_kernel(const PassParams P) {
+    const int r = blockIdx.y;
+    const int lpr = P.D / 8;
+    const int sub = threadIdx.x % lpr, rl = threadIdx.x / lpr, rpw = PT / lpr;
+    const int64_t nrows = (int64_t)P.max_new * P.Hkv;
+    const float ksc = *P.fscale, vsc = *P.fscale2;
+    for (int64_t row = (int64_t)blockIdx.x * rpw + rl; row < nrows; row += (int64_t)gridDim.x * rpw) {
+        int64_t src = 0, off = 0, soff = 0;
+        if (!store_row(P, r, row, src, off, soff)) continue;
+        float k[8], v[8];
+        load8(P.src, src + sub * 8, k);
+        load8(P.src2, src + sub * 8, v);
+        *(u32x2 *)((uint8_t *)P.dst + off + sub * 8) = u32x2{fp8x4(k, ksc), fp8x4(k + 4, ksc)};
+        *(u32x2 *)((uint8_t *)P.dst2 + off + sub * 8) = u32x2{fp8x4(v, vsc), fp8x4(v + 4, vsc)};
+    }
+}
+
 static dim3 pass_grid(const PassParams &p, int row_bytes) {
     const int lpr = row_bytes / 16;
     const int rpw = PT / lpr;
@@ -192,6 +299,24 @@ hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t s) {
 }
 hipError_t launch_gather(const PassParams &p, hipStream_t s) {
     hipLaunchKernelGGL(gather_kernel, pass_grid(p, p.D * p.elem_bytes), dim3(PT), 0, s, p);
+    return hipGetLastError();
+}
+
+static dim3 store_grid(const PassParams &p) {
+    const int rpw = PT / (p.D / 8);
+    int64_t x = ((int64_t)p.max_new * p.Hkv + rpw - 1) / rpw;
+    if (x > 65536) x = 65536;
+    if (x < 1) x = 1;
+    return dim3((uint32_t)x, (uint32_t)p.num_reqs);
+}
+hipError_t launch_store_int8(const PassParams &p, hipStream_t s) {
+    if (p.max_new <= 0) return hipSuccess;
+    hipLaunchKernelGGL(store_int8_kernel, store_grid(p), dim3(PT), 0, s, p);
+    return hipGetLastError();
+}
+hipError_t launch_store_fp8(const PassParams &p, hipStream_t s) {
+    if (p.max_new <= 0) return hipSuccess;
+    hipLaunchKernelGGL(store_fp8_kernel, store_grid(p), dim3(PT), 0, s, p);
     return hipGetLastError();
 }
 

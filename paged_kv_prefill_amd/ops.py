@@ -27,7 +27,8 @@ PA_MAX_SPLITS = 256
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
                 "pa_prefill_int8kv_splitkv", "pa_k_stats", "pa_k_quant",
-                "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_gather_kv",
+                "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_store_kv_int8", "pa_store_kv_fp8",
+                "pa_gather_kv",
                 "pa_peak_probe", "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
 
 
@@ -72,6 +73,8 @@ def lib():
             "pa_prefill_int8qk": [pa, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
             "pa_fp8_dense_dequant": [pa, vp, vp, vp, vp, i32, vp, vp, vp],
             "pa_gather_kv": [pa, vp, i32, vp, vp, vp],
+            "pa_store_kv_int8": [pa, vp, vp, vp, vp, vp, vp, vp],
+            "pa_store_kv_fp8": [pa, vp, vp, vp, vp, vp, vp, vp],
             "pa_peak_probe": [i32, i32, i32, vp, vp],
         }
         for name, argt in sig.items():
@@ -233,6 +236,16 @@ def pa_prefill_int8kv_splitkv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, o
                                            _p(out), dt, _p(lse), wp, wn, _stream(stream)),
            "pa_prefill_int8kv_splitkv")
     return out
+
+
+def pa_store_kv_int8(p: Paged, k_new, v_new, k_pool, v_pool, k_scales, v_scales, stream=None):
+    _check(lib().pa_store_kv_int8(C.byref(p.args()), _p(k_new), _p(v_new), _p(k_pool), _p(v_pool),
+                                  _p(k_scales), _p(v_scales), _stream(stream)), "pa_store_kv_int8")
+
+
+def pa_store_kv_fp8(p: Paged, k_new, v_new, k_scale, v_scale, k_pool, v_pool, stream=None):
+    _check(lib().pa_store_kv_fp8(C.byref(p.args()), _p(k_new), _p(v_new), _p(k_scale), _p(v_scale),
+                                 _p(k_pool), _p(v_pool), _stream(stream)), "pa_store_kv_fp8")
 
 
 def _kdtype(pool):

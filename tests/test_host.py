@@ -132,6 +132,20 @@ def test_split_kv_argument_errors():
     assert i8(C.byref(a), p, p, p, p, p, 4, p, None, p, 0, None, p, big, None) == ops.PA_ERR_NULL
 
 
+def test_store_argument_errors():
+    L = ops.lib()
+    a = _args()
+    p = C.c_void_p(4096)
+    odd = C.c_void_p(4100)
+    assert L.pa_store_kv_int8(C.byref(a), None, p, p, p, p, p, None) == ops.PA_ERR_NULL
+    assert L.pa_store_kv_int8(C.byref(a), p, p, p, p, None, p, None) == ops.PA_ERR_NULL
+    assert L.pa_store_kv_int8(C.byref(a), odd, p, p, p, p, p, None) == ops.PA_ERR_SHAPE
+    assert L.pa_store_kv_int8(C.byref(_args(cu_q_lens=None)), p, p, p, p, p, p, None) == ops.PA_ERR_NULL
+    assert L.pa_store_kv_fp8(C.byref(a), p, p, None, p, p, p, None) == ops.PA_ERR_NULL
+    assert L.pa_store_kv_fp8(C.byref(a), p, p, p, p, odd, p, None) == ops.PA_ERR_SHAPE
+    assert L.pa_store_kv_fp8(C.byref(_args(num_q_heads=3)), p, p, p, p, p, p, None) == ops.PA_ERR_SHAPE
+
+
 def _split_tiles(s, splits, t_full, n_tiles):
     """The documented key-range rule of the split-KV entry points."""
     se = 1 if t_full < 1 else min(splits, t_full)
