@@ -28,7 +28,18 @@ i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
 vp = C.c_void_p
 i64, i32, f32 = C.c_int64, C.c_int32, C.c_float
 
-KV_BF16, KV_INT8 = 0, 1
+KV_BF16, KV_INT8, KV_FP8 = 0, 1, 2
+
+
+def _kv_kind(pool):
+    return {np.dtype(np.int8): KV_INT8, np.dtype(np.uint8): KV_FP8}.get(pool.dtype, KV_BF16)
+
+
+def _scales(kind, s):
+    """fp8 pools carry one scale per tensor, passed as a length-1 array."""
+    if kind == KV_FP8 and s is not None:
+        return np.ascontiguousarray(np.atleast_1d(s), dtype=np.float32)
+    return s
 
 
 def load(path: str | None = None):
@@ -105,7 +116,8 @@ def prefill(block_table, cu_q_lens, ctx_lens, q, k_pool, v_pool, softmax_scale,
         rows = np.arange(int(cu_q[-1]), dtype=np.int32)
     rows = np.ascontiguousarray(rows, dtype=np.int32)
     out = np.empty((len(rows), hq, d), dtype=np.float64)
-    kind = KV_INT8 if k_pool.dtype == np.int8 else KV_BF16
+    kind = _kv_kind(k_pool)
+    k_scales, v_scales = _scales(kind, k_scales), _scales(kind, v_scales)
     if kind == KV_INT8:
         ssb, sst = bs * hkv, hkv
     else:
@@ -142,7 +154,8 @@ def prefill_lse(block_table, cu_q_lens, ctx_lens, q, k_pool, v_pool, softmax_sca
     hi = None if key_hi is None else np.ascontiguousarray(np.broadcast_to(key_hi, rows.shape), dtype=np.int32)
     out = np.empty((len(rows), hq, d), dtype=np.float64)
     lse = np.empty((len(rows), hq), dtype=np.float64)
-    kind = KV_INT8 if k_pool.dtype == np.int8 else KV_BF16
+    kind = _kv_kind(k_pool)
+    k_scales, v_scales = _scales(kind, k_scales), _scales(kind, v_scales)
     ssb, sst = (bs * hkv, hkv) if kind == KV_INT8 else (0, 0)
     sb, st, sh = _pool_strides(k_pool)
     rc = lib.oracle_prefill_lse(_ptr(bt), bt.shape[1], cu_q, ctx, len(ctx), bs, hq, hkv, d,

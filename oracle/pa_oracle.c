@@ -143,7 +143,10 @@ static int64_t scale_offset(const paged_view *pv, int64_t stride_sblock, int64_t
 
 /* ------------------------------------------------------------ attention */
 
-enum { KV_BF16 = 0, KV_INT8 = 1 };
+/* Pool formats: bf16 values; int8 codes with per-token-head scales; fp8
+ * e4m3fn codes with one scale per tensor (k_scales[0] / v_scales[0]), read as
+ * the pool's own values decode(code) * scale. */
+enum { KV_BF16 = 0, KV_INT8 = 1, KV_FP8 = 2 };
 
 static void set_threads(int n) {
 #ifdef _OPENMP
@@ -223,6 +226,10 @@ static int prefill_range(const int32_t *block_table, int64_t stride_bt,
                 if (kv_kind == KV_BF16) {
                     const uint16_t *kp = (const uint16_t *)k_pool + off;
                     for (int d = 0; d < D; ++d) dot += qv[d] * (double)bf16_bits_to_f32(kp[d]);
+                } else if (kv_kind == KV_FP8) {
+                    const uint8_t *kp = (const uint8_t *)k_pool + off;
+                    double sc = (double)k_scales[0];
+                    for (int d = 0; d < D; ++d) dot += qv[d] * ((double)e4m3fn_to_f32(kp[d]) * sc);
                 } else {
                     const int8_t *kp = (const int8_t *)k_pool + off;
                     double sc = (double)k_scales[scale_offset(&pv, stride_sblock, stride_stok, r, j, g)];
@@ -241,6 +248,10 @@ static int prefill_range(const int32_t *block_table, int64_t stride_bt,
                 if (kv_kind == KV_BF16) {
                     const uint16_t *vp = (const uint16_t *)v_pool + off;
                     for (int d = 0; d < D; ++d) acc[d] += e * (double)bf16_bits_to_f32(vp[d]);
+                } else if (kv_kind == KV_FP8) {
+                    const uint8_t *vp = (const uint8_t *)v_pool + off;
+                    double sc = (double)v_scales[0];
+                    for (int d = 0; d < D; ++d) acc[d] += e * ((double)e4m3fn_to_f32(vp[d]) * sc);
                 } else {
                     const int8_t *vp = (const int8_t *)v_pool + off;
                     double sc = (double)v_scales[scale_offset(&pv, stride_sblock, stride_stok, r, j, g)];

@@ -34,6 +34,9 @@ def dense_values(w, which):
         codes = getattr(w, which).astype(np.float64)
         sc = getattr(w, which + "_scales").astype(np.float64)
         return codes * sc[..., None]
+    if w.kv_format == "fp8":
+        dec = torch.from_numpy(getattr(w, which)).view(torch.float8_e4m3fn).double().numpy()
+        return dec * float(getattr(w, which + "_scale"))
     raise ValueError(w.kv_format)
 
 
@@ -162,6 +165,34 @@ def test_int8_kv_matches_sdpa_on_dequantised_values(orc):
     ours = run_oracle(orc, w)
     ref = sdpa_reference(w)
     assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+def test_fp8_pool_read_directly_matches_sdpa_on_decoded_values(orc):
+    """An fp8 pool read as decode(code) * scale equals SDPA on those values."""
+    w = synth.make_case(18, [6, 4], [19, 30], 5, 4, 2, 64, kv_format="fp8")
+    pools = synth.host_pools(w)
+    ours = orc.prefill(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
+                       w.softmax_scale, k_scales=w.k_scale, v_scales=w.v_scale)
+    assert np.max(np.abs(ours - sdpa_reference(w))) < 1e-12
+
+
+def test_fp8_direct_read_equals_dense_scratch_with_pow2_scale(orc):
+    """With power-of-two scales the bf16 scratch holds decode(code) * scale
+    exactly, so reading the pool directly and reading the scratch agree bit for
+    bit; with another scale they differ by the scratch's bf16 rounding only."""
+    w = synth.make_case(19, [5, 3], [40, 21], 8, 4, 2, 64, kv_format="fp8", num_blocks=12)
+    for ks, vs, exact in ((0.015625, 0.0078125, True), (w.k_scale, w.v_scale, False)):
+        pools = synth.host_pools(w)
+        direct = orc.prefill(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
+                             w.softmax_scale, k_scales=np.float32(ks), v_scales=np.float32(vs))
+        ksc, vsc = orc.fp8_dense_dequant(w.block_table, w.ctx_lens, pools["k"], pools["v"],
+                                         np.float32(ks), np.float32(vs), max_seq=40)
+        ident = np.arange(w.num_reqs, dtype=np.int32)[:, None]
+        dense = orc.prefill(ident, w.cu_q_lens, w.ctx_lens, w.q, ksc, vsc, w.softmax_scale)
+        if exact:
+            assert np.array_equal(direct, dense)
+        else:
+            assert 0 < np.max(np.abs(direct - dense)) < 1e-2
 
 
 def test_zero_query_gives_mean_of_visible_values(orc):
