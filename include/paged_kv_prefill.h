@@ -74,6 +74,7 @@ extern "C" {
 #define PA_ENTRY_PREFILL_BF16    1
 #define PA_ENTRY_PREFILL_INT8KV  2
 #define PA_ENTRY_PREFILL_INT8QK  3
+#define PA_ENTRY_PREFILL_FP8KV   4
 
 /* element types */
 #define PA_DTYPE_F32        0
@@ -112,6 +113,11 @@ typedef struct pa_paged_args {
  * lengths have changed since.  The call then skips the image and schedule
  * passes and launches the attention kernel alone. */
 #define PA_FLAG_IMAGES_READY 1
+/* pa_fp8_dense_dequant only: dequantise just the chunk's positions, the last
+ * Lq_r (cu_q_lens) of each context, into a scratch whose earlier positions
+ * earlier calls already filled (an incremental, persistent scratch).  Other
+ * entry points ignore it. */
+#define PA_FLAG_APPEND       2
 
 /*
  * pa_prefill_bf16 -- chunked-prefill attention over a bf16 paged pool.
@@ -189,6 +195,25 @@ int pa_prefill_int8kv_splitkv(const pa_paged_args *args, const void *q, const in
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_prefill_fp8kv -- attention straight over an fp8 e4m3fn pool with one
+ * scale per tensor, the A/B arm of the one-time dense dequant (vllm.cpp PR
+ * #3360, "What changed": its VT_ATTN_FP8_DENSE=0 switch keeps the per-read
+ * path for exactly this comparison).  The call's tile images are built from
+ * the fp8 codes directly: K as decoded values (exact in bf16) with the tensor
+ * scale applied to the logits, V as decoded values (exact in fp16) with the
+ * tensor scale applied to the output; then the attention runs as
+ * pa_prefill_int8kv.  K_j / V_j are thus the pool's own values
+ * decode(code) * scale, with no rounding of them at all (the dense scratch
+ * rounds each to bf16).
+ *   k_pool, v_pool    e4m3fn codes; k_scale, v_scale  device fp32 scalars
+ *   workspace         pa_workspace_bytes(args, PA_ENTRY_PREFILL_FP8KV)
+ */
+int pa_prefill_fp8kv(const pa_paged_args *args, const void *q, const uint8_t *k_pool,
+                     const uint8_t *v_pool, const float *k_scale, const float *v_scale, void *out,
+                     int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
  * pa_k_stats -- first pass of the int8-QK prefill (HyperQwen PR #109: the
  * K-stats kernel reads K through the block table).  For every context token
  * t < L_r and KV head g:   ks[cu_ctx[r] + t, g] = max_d |K| / 127  (fp32).
@@ -230,7 +255,7 @@ int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8
  * pa_workspace_bytes -- device workspace an attention entry point needs for
  * these arguments: n = num_reqs * ceil(max_ctx_len / 64) * num_kv_heads V tile
  * images of 144 * head_dim + 256 bytes (fp16 rows of 64 keys padded to 72,
- * plus scales), and for PA_ENTRY_PREFILL_INT8KV n more K tile images of
+ * plus scales), and for PA_ENTRY_PREFILL_INT8KV / _FP8KV n more K tile images of
  * 128 * head_dim + 256 bytes; then, from the next multiple of 256 bytes, the
  * work schedule: 4 bytes per attention workgroup, num_reqs * num_kv_heads *
  * ceil(max_q_len * (num_q_heads / num_kv_heads) / 128) rounded up to a
@@ -247,7 +272,8 @@ size_t pa_workspace_bytes(const pa_paged_args *args, int32_t entry);
  * unchanged).  For t < L_r:
  *     k_scratch[r, t, g, d] = bf16_rne(fp32(e4m3fn(code)) * (*k_scale))
  * and likewise for V.  k_scale / v_scale are DEVICE fp32 scalars (one scale per
- * tensor).  Positions t >= L_r of the scratch are not written.  Afterwards call
+ * tensor).  Positions t >= L_r of the scratch are not written; with
+ * PA_FLAG_APPEND only t >= L_r - Lq_r are (cu_q_lens required).  Afterwards call
  * pa_prefill_bf16 with block_size = max_seq, block_table row r = {r},
  * stride_block = max_seq * Hkv * D, stride_tok = Hkv * D, stride_head = D.
  */

@@ -38,7 +38,7 @@ int check_common(const pa_paged_args *a, int elem_bytes, bool needs_q) {
     if (a->max_ctx_len < 0 || a->max_q_len < 0 || (needs_q && a->max_q_len > a->max_ctx_len))
         return PA_ERR_SHAPE;
     if (a->causal != 0 && a->causal != 1) return PA_ERR_SHAPE;
-    if (a->flags & ~PA_FLAG_IMAGES_READY) return PA_ERR_SHAPE;
+    if (a->flags & ~(PA_FLAG_IMAGES_READY | PA_FLAG_APPEND)) return PA_ERR_SHAPE;
     if (!(a->softmax_scale > 0.0f) || a->softmax_scale == INFINITY) return PA_ERR_SHAPE;
     if (a->stride_block < 1 || a->stride_tok < 1 || a->stride_head < 1) return PA_ERR_SHAPE;
     // rows are read as 16-byte vectors: every row start must be 16-byte aligned
@@ -119,8 +119,8 @@ int64_t image_count(const pa_paged_args *a) {
 // per attention workgroup
 int64_t sched_offset(const pa_paged_args *a, int32_t entry) {
     const int64_t n = image_count(a);
-    const int64_t img = n * v_image_bytes(a->head_dim) +
-                        (entry == PA_ENTRY_PREFILL_INT8KV ? n * k_image_bytes(a->head_dim) : 0);
+    const bool k_img = entry == PA_ENTRY_PREFILL_INT8KV || entry == PA_ENTRY_PREFILL_FP8KV;
+    const int64_t img = n * v_image_bytes(a->head_dim) + (k_img ? n * k_image_bytes(a->head_dim) : 0);
     return (img + 255) / 256 * 256;
 }
 
@@ -229,7 +229,7 @@ int prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, cons
     ImageParams ip = image_params(a, workspace, KIND_BF16);
     ip.src = v_pool;
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
-    if (build && (rc = launched(launch_images(ip, false, false, stream)))) return rc;
+    if (build && (rc = launched(launch_images(ip, IMG_BF16, false, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.sched = so ? nullptr : schedule_ptr(a, PA_ENTRY_PREFILL_BF16, workspace);
     if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
@@ -258,7 +258,7 @@ int prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
     ip.src2 = k_pool;
     ip.src2_scales = k_scales;
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
-    if (build && (rc = launched(launch_images(ip, true, true, stream)))) return rc;
+    if (build && (rc = launched(launch_images(ip, IMG_I8, true, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.sched = so ? nullptr : schedule_ptr(a, PA_ENTRY_PREFILL_INT8KV, workspace);
     if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
@@ -303,6 +303,34 @@ int pa_prefill_int8kv_splitkv(const pa_paged_args *a, const void *q, const int8_
     const SplitOut so{num_splits, o_part, lse_part, lse};
     return prefill_int8kv(a, q, k_pool, v_pool, k_scales, v_scales, &so, out, out_dtype, workspace,
                           workspace_bytes, stream);
+}
+
+int pa_prefill_fp8kv(const pa_paged_args *a, const void *q, const uint8_t *k_pool,
+                     const uint8_t *v_pool, const float *k_scale, const float *v_scale, void *out,
+                     int32_t out_dtype, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_common(a, 1, true);
+    if (rc) return rc;
+    if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (!k_pool || !v_pool || !k_scale || !v_scale) return PA_ERR_NULL;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    if ((rc = check_workspace(a, PA_ENTRY_PREFILL_FP8KV, workspace, workspace_bytes))) return rc;
+    ImageParams ip = image_params(a, workspace, KIND_I8KV);
+    ip.src = v_pool;
+    ip.src2 = k_pool;
+    ip.fscale2 = k_scale;
+    const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
+    if (build && (rc = launched(launch_images(ip, IMG_FP8, true, stream)))) return rc;
+    AttnParams p = attn_params(a);
+    p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_FP8KV, workspace);
+    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    p.q = q;
+    p.v_img = (const char *)ip.dst;
+    p.k_img = (const char *)ip.dst2;
+    p.img_tiles = ip.tiles;
+    p.oscale = v_scale;   // the V image holds decoded values; the tensor scale multiplies O
+    p.out = out;
+    return launched(launch_attention(KIND_I8KV, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
+                                     a->max_q_len, stream));
 }
 
 int pa_k_stats(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
@@ -360,7 +388,7 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     ip.src = v_pool;
     ip.src_scales = v_scales;
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
-    if (build && (rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8, false, stream)))) return rc;
+    if (build && (rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8 ? IMG_I8 : IMG_BF16, false, stream)))) return rc;
     AttnParams p = attn_params(a);
     p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_INT8QK, workspace);
     if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
@@ -377,7 +405,7 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
 
 size_t pa_workspace_bytes(const pa_paged_args *a, int32_t entry) {
     if (entry != PA_ENTRY_PREFILL_BF16 && entry != PA_ENTRY_PREFILL_INT8KV &&
-        entry != PA_ENTRY_PREFILL_INT8QK)
+        entry != PA_ENTRY_PREFILL_INT8QK && entry != PA_ENTRY_PREFILL_FP8KV)
         return 0;
     if (check_common(a, 1, false) != PA_OK) return 0;
     return (size_t)workspace_need(a, entry);
@@ -392,7 +420,12 @@ int pa_fp8_dense_dequant(const pa_paged_args *a, const uint8_t *k_pool, const ui
     if (max_seq < 1 || max_seq < a->max_ctx_len) return PA_ERR_SHAPE;
     if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_scratch) || !aligned16(v_scratch))
         return PA_ERR_SHAPE;
+    const bool append = (a->flags & PA_FLAG_APPEND) != 0;
+    if (append && !a->cu_q_lens) return PA_ERR_NULL;
+    if (append && a->max_q_len > a->max_ctx_len) return PA_ERR_SHAPE;
     PassParams p = pass_params(a);
+    p.cu_new = append ? a->cu_q_lens : nullptr;
+    p.max_new = a->max_q_len;
     p.src = k_pool;
     p.src2 = v_pool;
     p.fscale = k_scale;

@@ -768,7 +768,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // ---- epilogue: O / l, row of this lane's column; a split-KV partial also
     // records its range's log-sum-exp, ln(sum_j e^{s_j}) = ln2 (m_run + log2 l)
     const float l_tot = sum_halves(l_run);
-    const float inv = 1.0f / l_tot;
+    const float inv = (P.oscale ? *P.oscale : 1.0f) / l_tot;
     if (!col_valid) return;
     int64_t orow = ((int64_t)(q0 + tok) * P.Hq + h) * D;
     float *out_f32 = (float *)P.out;

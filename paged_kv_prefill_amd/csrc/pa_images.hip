@@ -18,7 +18,12 @@
 // per-token-head scale, rounded once to fp16), so the attention kernel's PV
 // takes them like bf16 V; the scales also go to the image's scale vector.
 // K codes (the exact-QK arm's K image) are kept as codes, exact in bf16, with
-// their scales.  Keys at or past the context length are zero (scale 0).
+// their scales.  An fp8 e4m3fn pool read directly is handled the same way,
+// without rounding: every e4m3fn value is exact in fp16 and in bf16, so the V
+// image holds the decoded values (the attention multiplies its output by the
+// V tensor's scale) and the K image the decoded values with the K tensor's
+// scale as every key's scale.
+// Keys at or past the context length are zero (scale 0).
 #include "pa_device.h"
 #include "pa_kernels.h"
 #include "pa_layout.h"
@@ -48,12 +53,21 @@ __device__ __forceinline__ bool img_tile(const ImageParams &P, int &t, int &g, i
     return t * TILE_KEYS < L;
 }
 
+// e4m3fn codes -> fp32 with gfx950's converter (OCP E4M3)
+__device__ __forceinline__ float fp8_at(uint32_t word, int b) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);   // bytes 0, 1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);    // bytes 2, 3
+    return (b >> 1) ? hi[b & 1] : lo[b & 1];
+}
+
 // V^T image: [D][72] fp16 (64 columns in MFMA-position order + zero padding)
 // + 64 scales in position order.  One unit = 4 consecutive positions (4
 // consecutive columns) x one 16-byte chunk of the source row; its 4 x 8 (bf16)
-// or 4 x 16 (int8) values go to LDS as 8-byte groups of the 4 columns of one dim.
-template <int D, bool SRC_I8>
+// or 4 x 16 (int8, fp8) values go to LDS as 8-byte groups of the 4 columns of
+// one dim.
+template <int D, int SRC>
 __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
+    constexpr bool SRC_I8 = SRC != IMG_BF16;   // one byte per element
     constexpr int CPR = (SRC_I8 ? D : 2 * D) / 16;
     constexpr int UNITS = 16 * CPR;
     constexpr int V_BYTES = vt_tile_bytes(D);
@@ -75,7 +89,7 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
             const bool ok = key < L && img_row(P, r, key, g, off, soff);
             if (SRC_I8) {
                 w[j] = ok ? *(const u32x4 *)((const int8_t *)P.src + off + dc * 16) : u32x4{0, 0, 0, 0};
-                s[j] = ok ? P.src_scales[soff] : 0.f;
+                s[j] = ok ? (SRC == IMG_FP8 ? 1.0f : P.src_scales[soff]) : 0.f;
             } else {
                 w[j] = ok ? *(const u32x4 *)((const __bf16 *)P.src + off + dc * 8) : u32x4{0, 0, 0, 0};
                 s[j] = 0.f;
@@ -87,7 +101,9 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
             for (int e = 0; e < 16; ++e) {
                 float x[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = (float)(int8_t)((w[j][e >> 2] >> ((e & 3) * 8)) & 0xff) * s[j];
+                for (int j = 0; j < 4; ++j)
+                    x[j] = (SRC == IMG_FP8 ? fp8_at(w[j][e >> 2], e & 3)
+                                           : (float)(int8_t)((w[j][e >> 2] >> ((e & 3) * 8)) & 0xff)) * s[j];
                 *(u32x2 *)(img + vt_off(dc * 16 + e, slot)) =
                     u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
             }
@@ -112,8 +128,10 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
     for (int c = tid; c < CHUNKS; c += IT) *(u32x4 *)(dst + c * 16) = *(const u32x4 *)(img + c * 16);
 }
 
-// K image of an int8 pool: [64][D] bf16 codes (exact) in key order + 64 scales.
-template <int D>
+// K image of an int8 pool: [64][D] bf16 codes (exact) in key order + 64
+// scales; of an fp8 pool: the decoded values (exact in bf16) + the tensor
+// scale for every key.
+template <int D, bool FP8>
 __global__ __launch_bounds__(IT) void k_image_kernel(const ImageParams P) {
     constexpr int CPR = D / 16;                      // source chunks (16 codes) per row
     int t, g, r, L;
@@ -134,40 +152,48 @@ __global__ __launch_bounds__(IT) void k_image_kernel(const ImageParams P) {
             for (int q = 0; q < 4; ++q) {
                 const uint32_t word = w[half * 2 + (q >> 1)];
                 const int sh = (q & 1) * 16;
-                o[q] = pack_bf16x2((float)(int8_t)((word >> sh) & 0xff),
-                                   (float)(int8_t)((word >> (sh + 8)) & 0xff));
+                if constexpr (FP8)
+                    o[q] = pack_bf16x2(fp8_at(word, (q & 1) * 2), fp8_at(word, (q & 1) * 2 + 1));
+                else
+                    o[q] = pack_bf16x2((float)(int8_t)((word >> sh) & 0xff),
+                                       (float)(int8_t)((word >> (sh + 8)) & 0xff));
             }
             *(u32x4 *)(dst + row * (D * 2) + (dc * 2 + half) * 16) = o;
         }
-        if (dc == 0) scl[row] = ok ? P.src_scales[soff] : 0.f;
+        if (dc == 0) scl[row] = ok ? (FP8 ? *P.fscale2 : P.src_scales[soff]) : 0.f;
     }
 }
 
 template <int D>
-static hipError_t launch_images_d(const ImageParams &p, bool v_int8, bool k_image, hipStream_t s) {
+static hipError_t launch_images_d(const ImageParams &p, int fmt, bool k_image, hipStream_t s) {
     dim3 grid((uint32_t)p.tiles, (uint32_t)p.Hkv, (uint32_t)p.num_reqs);
     ImageParams pv = p;
-    if (v_int8) {
-        hipLaunchKernelGGL((v_image_kernel<D, true>), grid, dim3(IT), 0, s, pv);
-    } else {
-        hipLaunchKernelGGL((v_image_kernel<D, false>), grid, dim3(IT), 0, s, pv);
-    }
+    if (fmt == IMG_I8)
+        hipLaunchKernelGGL((v_image_kernel<D, IMG_I8>), grid, dim3(IT), 0, s, pv);
+    else if (fmt == IMG_FP8)
+        hipLaunchKernelGGL((v_image_kernel<D, IMG_FP8>), grid, dim3(IT), 0, s, pv);
+    else
+        hipLaunchKernelGGL((v_image_kernel<D, IMG_BF16>), grid, dim3(IT), 0, s, pv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !k_image) return e;
     ImageParams pk = p;
     pk.src = p.src2;
     pk.src_scales = p.src2_scales;
     pk.dst = p.dst2;
-    hipLaunchKernelGGL((k_image_kernel<D>), grid, dim3(IT), 0, s, pk);
+    if (fmt == IMG_FP8)
+        hipLaunchKernelGGL((k_image_kernel<D, true>), grid, dim3(IT), 0, s, pk);
+    else
+        hipLaunchKernelGGL((k_image_kernel<D, false>), grid, dim3(IT), 0, s, pk);
     return hipGetLastError();
 }
 
-hipError_t launch_images(const ImageParams &p, bool v_int8, bool k_image, hipStream_t s) {
+hipError_t launch_images(const ImageParams &p, int fmt, bool k_image, hipStream_t s) {
     if (p.tiles <= 0) return hipSuccess;
+    if (fmt != IMG_BF16 && fmt != IMG_I8 && fmt != IMG_FP8) return hipErrorInvalidValue;
     switch (p.D) {
-        case 64: return launch_images_d<64>(p, v_int8, k_image, s);
-        case 128: return launch_images_d<128>(p, v_int8, k_image, s);
-        case 256: return launch_images_d<256>(p, v_int8, k_image, s);
+        case 64: return launch_images_d<64>(p, fmt, k_image, s);
+        case 128: return launch_images_d<128>(p, fmt, k_image, s);
+        case 256: return launch_images_d<256>(p, fmt, k_image, s);
         default: return hipErrorInvalidValue;
     }
 }

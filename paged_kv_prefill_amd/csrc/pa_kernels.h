@@ -41,6 +41,7 @@ struct AttnParams {
     int32_t splits;             // >= 1
     float *o_part;              // [sum Lq, Hq, splits, D] fp32, or null
     float *lse_part;            // [sum Lq, Hq, splits] fp32 (natural log)
+    const float *oscale;        // device scalar multiplying O (a V tensor scale), or null
 };
 
 // Merge of split-KV partials into the output (pa_merge in pa_attention.hip).
@@ -107,7 +108,10 @@ struct ImageParams {
     const float *src2_scales;
     void *dst;                  // V images
     void *dst2;                 // K images
+    const float *fscale2;       // fp8 pools: the K tensor's scale (device scalar)
 };
+
+enum ImageSrc { IMG_BF16 = 0, IMG_I8 = 1, IMG_FP8 = 2 };   // pool element format of an image pass
 
 // launchers: return hipError_t of the launch
 hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnParams &p,
@@ -116,7 +120,7 @@ hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnPar
 hipError_t launch_merge(const MergeParams &p, bool out_bf16, int32_t max_q_len, hipStream_t stream);
 // key rows per 1 KB K copy of an attention kind (fixes the tile's key order)
 int attn_rows_per_copy(int kind, int head_dim);
-hipError_t launch_images(const ImageParams &p, bool v_int8, bool k_image, hipStream_t stream);
+hipError_t launch_images(const ImageParams &p, int fmt, bool k_image, hipStream_t stream);
 // the attention work schedule for these lengths (into p.sched)
 hipError_t launch_schedule(const AttnParams &p, int32_t max_q_len, hipStream_t stream);
 hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);

@@ -135,10 +135,18 @@ __global__ __launch_bounds__(PT) void fp8_dequant_kernel(const PassParams P) {
     if (!request_ok(P, r, L) || L > P.max_seq) return;
     const int lpr = P.D / 16;   // 16 fp8 codes per lane
     const int sub = threadIdx.x % lpr, rl = threadIdx.x / lpr, rpw = PT / lpr;
+    // all positions, or (append) only the chunk's: the last Lq of the context
+    int first = 0;
+    if (P.cu_new) {
+        const int n = P.cu_new[r + 1] - P.cu_new[r];
+        if (n < 0 || n > L) return;
+        first = L - n;
+    }
     const int64_t nrows = (int64_t)L * P.Hkv;
     const float ksc = *P.fscale, vsc = *P.fscale2;
     const int64_t dst0 = (int64_t)r * P.max_seq * P.Hkv;
-    for (int64_t row = (int64_t)blockIdx.x * rpw + rl; row < nrows; row += (int64_t)gridDim.x * rpw) {
+    for (int64_t row = (int64_t)first * P.Hkv + (int64_t)blockIdx.x * rpw + rl; row < nrows;
+         row += (int64_t)gridDim.x * rpw) {
         const int t = (int)((uint32_t)row / (uint32_t)P.Hkv), g = (int)((uint32_t)row % (uint32_t)P.Hkv);
         int64_t off = 0, soff = 0;
         const bool ok = pass_row(P, r, t, g, off, soff);
@@ -294,7 +302,9 @@ hipError_t launch_k_quant(const PassParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(fp8_dequant_kernel, pass_grid(p, p.D), dim3(PT), 0, s, p);
+    PassParams g = p;
+    if (p.cu_new) g.max_ctx = p.max_new;   // append: the grid covers the chunk's rows only
+    hipLaunchKernelGGL(fp8_dequant_kernel, pass_grid(g, p.D), dim3(PT), 0, s, p);
     return hipGetLastError();
 }
 hipError_t launch_gather(const PassParams &p, hipStream_t s) {

@@ -20,13 +20,15 @@ LIB_PATH = os.path.join(HERE, "libpaged_kv_prefill.so")
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH, PA_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
 PA_ERR_WORKSPACE = -6
 PA_ENTRY_PREFILL_BF16, PA_ENTRY_PREFILL_INT8KV, PA_ENTRY_PREFILL_INT8QK = 1, 2, 3
+PA_ENTRY_PREFILL_FP8KV = 4
 PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_INT8, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 PA_FLAG_IMAGES_READY = 1
+PA_FLAG_APPEND = 2
 
 PA_MAX_SPLITS = 256
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
-                "pa_prefill_int8kv_splitkv", "pa_k_stats", "pa_k_quant",
+                "pa_prefill_int8kv_splitkv", "pa_prefill_fp8kv", "pa_k_stats", "pa_k_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_store_kv_int8", "pa_store_kv_fp8",
                 "pa_gather_kv",
                 "pa_peak_probe", "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
@@ -67,6 +69,7 @@ def lib():
             "pa_prefill_bf16": [pa, vp, vp, vp, vp, i32, vp, sz, vp],
             "pa_prefill_int8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
             "pa_prefill_bf16_splitkv": [pa, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
+            "pa_prefill_fp8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
             "pa_prefill_int8kv_splitkv": [pa, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
             "pa_k_stats": [pa, vp, i32, vp, vp, vp, vp],
             "pa_k_quant": [pa, vp, i32, vp, vp, vp, vp, vp],
@@ -200,6 +203,16 @@ def pa_prefill_int8kv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, out, ws=N
     _check(lib().pa_prefill_int8kv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(k_scales),
                                    _p(v_scales), _p(out), dt, wp, wn, _stream(stream)),
            "pa_prefill_int8kv")
+    return out
+
+
+def pa_prefill_fp8kv(p: Paged, q, k_pool, v_pool, k_scale, v_scale, out, ws=None, stream=None):
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    ws, wp, wn = _ws(p, PA_ENTRY_PREFILL_FP8KV, ws)
+    _check(lib().pa_prefill_fp8kv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(k_scale),
+                                  _p(v_scale), _p(out), dt, wp, wn, _stream(stream)),
+           "pa_prefill_fp8kv")
     return out
 
 

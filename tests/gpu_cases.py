@@ -141,6 +141,12 @@ class DevCase:
         ops.pa_prefill_bf16(ops.scratch_view(p, max_seq, DEV), self.q, ksc, vsc, o)
         return o, ksc, vsc
 
+    def run_fp8kv(self, which=0, out_dtype=torch.float32):
+        o = self.out(out_dtype)
+        ops.pa_prefill_fp8kv(self.paged(which), self.q, self.k_pool, self.v_pool, self.k_scale,
+                             self.v_scale, o)
+        return o
+
     def gather(self, pool, which=0):
         w = self.w
         dense = torch.empty((int(w.ctx_lens.sum()), w.num_kv_heads, w.head_dim), dtype=pool.dtype,

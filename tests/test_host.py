@@ -68,7 +68,7 @@ BAD = [
     (dict(causal=2), ops.PA_ERR_SHAPE),
     (dict(stride_tok=130), ops.PA_ERR_SHAPE),
     (dict(max_ctx_len=2 ** 30, max_q_len=8), ops.PA_ERR_TOO_LARGE),
-    (dict(flags=2), ops.PA_ERR_SHAPE),
+    (dict(flags=4), ops.PA_ERR_SHAPE),
 ]
 
 
@@ -130,6 +130,20 @@ def test_split_kv_argument_errors():
     assert i8(C.byref(a), p, p, p, p, p, 0, p, p, p, 0, None, p, big, None) == ops.PA_ERR_SHAPE
     assert i8(C.byref(a), p, p, p, None, p, 4, p, p, p, 0, None, p, big, None) == ops.PA_ERR_NULL
     assert i8(C.byref(a), p, p, p, p, p, 4, p, None, p, 0, None, p, big, None) == ops.PA_ERR_NULL
+
+
+def test_fp8kv_and_append_argument_errors():
+    L = ops.lib()
+    a = _args()
+    p = C.c_void_p(4096)
+    big = 1 << 40
+    assert L.pa_prefill_fp8kv(C.byref(a), p, p, p, None, p, p, 0, p, big, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_fp8kv(C.byref(a), p, p, p, p, p, p, 0, p, 16, None) == ops.PA_ERR_WORKSPACE
+    assert L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_FP8KV) == \
+        L.pa_workspace_bytes(C.byref(a), ops.PA_ENTRY_PREFILL_INT8KV)
+    ap = _args(flags=ops.PA_FLAG_APPEND, cu_q_lens=None)
+    assert L.pa_fp8_dense_dequant(C.byref(ap), p, p, p, p, 16, p, p, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16(C.byref(_args(flags=4)), p, p, p, p, 0, p, big, None) == ops.PA_ERR_SHAPE
 
 
 def test_store_argument_errors():
