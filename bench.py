@@ -351,8 +351,9 @@ def arm_splitkv(steps, warmup):
     context) whose 32 column tiles alone would leave most CUs idle, plain
     entry against 8 key splits; (2) spec-decode verify, 8 drafted tokens at a
     60,000-token context (int8 per-token-head and bf16 KV) with 32 splits,
-    whole calls (V image pass + attention + merge) and attention + merge
-    alone (images reused)."""
+    whole calls (V image pass + attention + merge), attention + merge alone
+    (images reused), and decode-loop steps (PA_FLAG_APPEND: only the last
+    tile's images rebuilt)."""
     res = {}
     w = synth.config_bigpool_bf16()
     lq = 256
@@ -399,11 +400,17 @@ def arm_splitkv(steps, warmup):
                                                          out, S, o_part, lse_part, None, ws)
         (t_call,), _ = time_launches([lambda: f(p)], steps, warmup)
         (t_ready,), _ = time_launches([lambda: f(pr)], steps, warmup)
+        # a verify step of a decode loop: the images of the tiles before the 8
+        # new tokens come from the previous step (same workspace), the rest are rebuilt
+        pap = P.paged()
+        pap.flags = ops.PA_FLAG_APPEND
+        (t_app,), _ = time_launches([lambda: f(pap)], steps, warmup)
         L, hkv, d = int(w.ctx_lens[0]), w.num_kv_heads, w.head_dim
         # algorithmic bytes: every K and V element (and int8 scale) of the context read once
         kv_bytes = 2 * L * hkv * d * (1 if fmt == "int8" else 2) + (2 * L * hkv * 4 if fmt == "int8" else 0)
         res[f"verify_60k_{fmt}"] = {
-            "splits": S, "ms_call": t_call, "ms_images_ready": t_ready,
+            "splits": S, "ms_call": t_call, "ms_images_ready": t_ready, "ms_append": t_app,
+            "gbs_append": kv_bytes / t_app * 1e-6,
             "kv_bytes": kv_bytes, "gbs_call": kv_bytes / t_call * 1e-6,
             "gbs_images_ready": kv_bytes / t_ready * 1e-6,
             "hbm_frac_images_ready": kv_bytes / t_ready * 1e-6 / PEAK_HBM_GBS}

@@ -113,10 +113,17 @@ typedef struct pa_paged_args {
  * lengths have changed since.  The call then skips the image and schedule
  * passes and launches the attention kernel alone. */
 #define PA_FLAG_IMAGES_READY 1
-/* pa_fp8_dense_dequant only: dequantise just the chunk's positions, the last
- * Lq_r (cu_q_lens) of each context, into a scratch whose earlier positions
- * earlier calls already filled (an incremental, persistent scratch).  Other
- * entry points ignore it. */
+/* Incremental calls over a context that only grew by this call's chunk (a
+ * decode or spec-decode verify loop).
+ *   pa_fp8_dense_dequant: dequantise just the chunk's positions, the last
+ *     Lq_r (cu_q_lens) of each context, into a scratch whose earlier positions
+ *     earlier calls already filled (an incremental, persistent scratch).
+ *   attention entry points: rebuild only the tile images from the one holding
+ *     each request's first chunk position on; the earlier tiles are taken from
+ *     the workspace as an earlier call left them.  That call must have used
+ *     the same entry point, workspace, num_reqs, max_ctx_len, head geometry
+ *     and pools, and the pool rows before the chunk must be unchanged since.
+ *   The writers ignore it. */
 #define PA_FLAG_APPEND       2
 
 /*

@@ -163,6 +163,7 @@ ImageParams image_params(const pa_paged_args *a, void *ws, int kind) {
     p.dst = ws;
     p.v_rpi = attn_rows_per_copy(kind, a->head_dim);
     p.dst2 = (char *)ws + image_count(a) * v_image_bytes(a->head_dim);
+    p.cu_new = (a->flags & PA_FLAG_APPEND) ? a->cu_q_lens : nullptr;
     return p;
 }
 

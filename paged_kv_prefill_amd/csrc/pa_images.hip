@@ -50,6 +50,10 @@ __device__ __forceinline__ bool img_tile(const ImageParams &P, int &t, int &g, i
     r = blockIdx.z;
     L = P.ctx_lens[r];
     if (L <= 0 || L > P.max_ctx || (int64_t)(L - 1) / P.block_size >= P.stride_bt) return false;
+    if (P.cu_new) {   // append: tiles wholly before the chunk are already in place
+        const int n = P.cu_new[r + 1] - P.cu_new[r];
+        if (n < 0 || n > L || t < (L - n) / TILE_KEYS) return false;
+    }
     return t * TILE_KEYS < L;
 }
 

@@ -109,6 +109,9 @@ struct ImageParams {
     void *dst;                  // V images
     void *dst2;                 // K images
     const float *fscale2;       // fp8 pools: the K tensor's scale (device scalar)
+    // append: only the tiles from the one holding each request's first chunk
+    // position on are rebuilt (cu_q: chunk prefix sums), the rest are kept
+    const int32_t *cu_new;
 };
 
 enum ImageSrc { IMG_BF16 = 0, IMG_I8 = 1, IMG_FP8 = 2 };   // pool element format of an image pass
