@@ -80,8 +80,14 @@ constexpr float RESCALE_SLACK = 8.0f;   // lazy-rescale threshold, log2 units
 #ifndef PA_PV_IN_A
 #define PA_PV_IN_A 0
 #endif
+// the int8-QK arm's phase A has half as many QK MFMAs for the same exponentials,
+// so it takes PV MFMAs into phase A as well (measured: 5 % faster than none)
+#ifndef PA_PV_IN_A_QK8
+#define PA_PV_IN_A_QK8 48
+#endif
 constexpr int QK_AHEAD = PA_QK_AHEAD;
 constexpr int PV_IN_A = PA_PV_IN_A;      // PV MFMAs in phase A per 24 of its PV-capable slots
+constexpr int PV_IN_A_QK8 = PA_PV_IN_A_QK8;
 constexpr int PV_AHEAD = PA_PV_AHEAD;
 #define PA_FENCE() __builtin_amdgcn_sched_barrier(0)
 // every helper lambda of the kernel is inlined: an outlined one takes the
@@ -172,6 +178,20 @@ __device__ __forceinline__ void barrier_lds_after_copies() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
+}
+
+// Phase A of a step issues, in slot m (0 <= m < nq), exponentials of elements
+// [32 m / nq, 32 (m+1) / nq) of the current tile and then, from slot lag on,
+// PV MFMAs [(m - lag) npa / (nq - lag), (m - lag + 1) npa / (nq - lag)).  PV
+// MFMA n reads P key step n / db, i.e. elements 8 (n / db) .. 8 (n / db) + 7:
+// each must be computed in the same or an earlier slot.
+__host__ __device__ constexpr bool pv_in_a_ready(int nq, int lag, int npa, int db) {
+    for (int m = lag; m < nq; ++m)
+        for (int n = (m - lag) * npa / (nq - lag); n < (m - lag + 1) * npa / (nq - lag); ++n) {
+            const int last = 8 * (n / db) + 7;     // last element of the key step
+            if (last >= (m + 1) * 32 / nq) return false;
+        }
+    return true;
 }
 
 // FAST (paged K only, chosen on the host): block_size a multiple of 16, so no
@@ -572,7 +592,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     static_assert(C::DB >= LAG, "P key step st is ready by PV MFMA st * DB");
     // PV MFMAs spread over phase A's slots LAG.. (the rest go to phase B, where
     // they carry tile kt+1's post-processing)
-    constexpr int NPA = (PV_IN_A * (NQ - LAG)) / 24 < NP ? (PV_IN_A * (NQ - LAG)) / 24 : NP;
+    constexpr int PVA = C::QK8 ? PV_IN_A_QK8 : PV_IN_A;
+    constexpr int NPA = (PVA * (NQ - LAG)) / 24 < NP ? (PVA * (NQ - LAG)) / 24 : NP;
+    // phase B keeps at least one PV MFMA: its slots carry tile kt+1's post-processing
+    static_assert(NP - NPA >= 1, "phase B needs a slot");
+    static_assert(pv_in_a_ready(NQ, LAG, NPA, C::DB), "a phase-A PV MFMA precedes its P");
     auto rdK = [&](const char *kr, int m) PA_INL -> u32x4 {
         return *(const u32x4 *)(kr + (m & 1) * C::KB_STEP + (m >> 1) * 32);
     };
