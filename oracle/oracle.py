@@ -36,8 +36,11 @@ def _kv_kind(pool):
 
 
 def _scales(kind, s):
-    """fp8 pools carry one scale per tensor, passed as a length-1 array."""
-    if kind == KV_FP8 and s is not None:
+    """fp8 pools carry one scale per tensor, passed as a length-1 array; int8
+    pools one per (block, slot, KV head).  Both kinds require them."""
+    if kind != KV_BF16 and s is None:
+        raise ValueError("an int8 or fp8 pool needs its scales")
+    if kind == KV_FP8:
         return np.ascontiguousarray(np.atleast_1d(s), dtype=np.float32)
     return s
 

@@ -185,6 +185,7 @@ static int prefill_range(const int32_t *block_table, int64_t stride_bt,
                          double *lse) {
     if (num_q_heads % num_kv_heads != 0 || block_size < 1 || head_dim < 1)
         return -1;
+    if (kv_kind != KV_BF16 && (!k_scales || !v_scales)) return -1;   /* scaled pools */
     paged_view pv = {block_table, stride_bt, block_size, stride_block, stride_tok, stride_head};
     const int group = num_q_heads / num_kv_heads;
     const int D = head_dim;
@@ -325,6 +326,7 @@ int oracle_prefill_int8qk(const int32_t *block_table, int64_t stride_bt,
                           int32_t num_threads, double *out) {
     if (num_q_heads % num_kv_heads != 0 || block_size < 1 || head_dim < 1)
         return -1;
+    if (v_kind != 0 && !v_scales) return -1;   /* an int8 V pool needs its scales */
     paged_view pv = {block_table, stride_bt, block_size, stride_block, stride_tok, stride_head};
     const int group = num_q_heads / num_kv_heads;
     const int D = head_dim;

@@ -58,6 +58,7 @@ SMALL = [
     (106, [33, 1], [100, 9], 4, 2, 2, 64, False),
     (107, [257], [1500], 64, 24, 4, 256, True),
     (108, [200, 3, 129], [200, 70, 4000], 880, 8, 8, 128, True),
+    (109, [0, 40, 0, 17], [50, 40, 3, 900], 16, 4, 2, 64, True),   # requests with no chunk
 ]
 IDS = [f"s{c[0]}" for c in SMALL]
 

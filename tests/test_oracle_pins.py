@@ -145,6 +145,25 @@ def test_batched_chunks_match_masked_sdpa(orc):
     assert np.max(np.abs(ours - ref)) < 1e-12
 
 
+def test_empty_chunks_match_masked_sdpa(orc):
+    """Requests with no chunk this call (Lq = 0) give no rows and leave the
+    other requests' rows as they are."""
+    w = synth.make_case(7, [0, 7, 0, 5], [12, 30, 3, 40], 4, 4, 2, 64)
+    ours = run_oracle(orc, w)
+    assert ours.shape[0] == 12
+    ref = sdpa_reference(w)
+    assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_scaled_pools_require_their_scales(orc, fmt):
+    w = synth.make_case(8, [3], [9], 4, 2, 1, 64, kv_format=fmt)
+    pools = synth.host_pools(w)
+    with pytest.raises(ValueError):
+        orc.prefill(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
+                    w.softmax_scale)
+
+
 def test_tiny_config_matches_masked_sdpa(orc):
     w = synth.config_tiny()
     assert w.block_table.tolist() == [[2, 4, 3]]
