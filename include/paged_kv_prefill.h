@@ -344,6 +344,29 @@ int pa_gather_kv(const pa_paged_args *args, const void *pool, int32_t elem_bytes
  */
 int pa_peak_probe(int32_t dtype, int32_t workgroups, int32_t iters, float *out, hipStream_t stream);
 
+/*
+ * pa_test_inject_failure -- test seam for the error path of the multi-kernel
+ * entry points (the pattern of vllm.cpp PR #3360's tests, which inject
+ * failures at the steps of the fp8 dense path and check that nothing is
+ * retained).  Arms a one-shot failure: the next launch of the given stage, in
+ * any entry point, is not enqueued and its call returns PA_ERR_LAUNCH, with
+ * the stages after it not enqueued either; the stages before it were enqueued
+ * as usual.  The seam is process-wide and not thread-safe; argument errors are
+ * still reported first.
+ *   stage: PA_STAGE_NONE (disarm), PA_STAGE_IMAGES (tile-image pass),
+ *   PA_STAGE_SCHEDULE (work schedule), PA_STAGE_ATTENTION, PA_STAGE_MERGE
+ *   (split-KV merge), PA_STAGE_PASS (K stats, K quant, fp8 dequant, gather,
+ *   quantise-on-store).
+ * Returns PA_OK, or PA_ERR_SHAPE for an unknown stage.
+ */
+#define PA_STAGE_NONE       0
+#define PA_STAGE_IMAGES     1
+#define PA_STAGE_SCHEDULE   2
+#define PA_STAGE_ATTENTION  3
+#define PA_STAGE_MERGE      4
+#define PA_STAGE_PASS       5
+int pa_test_inject_failure(int32_t stage);
+
 /* Human-readable text of a status code (static storage). */
 const char *pa_status_string(int32_t status);
 

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <atomic>
 #include <stdint.h>
 
 #include "pa_kernels.h"
@@ -110,6 +111,18 @@ int check_scales(const pa_paged_args *a, const float *s) {
 
 int launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+// pa_test_inject_failure's one-shot stage: its next launch is not made
+std::atomic<int32_t> g_fail_stage{PA_STAGE_NONE};
+
+template <typename F>
+int launch_stage(int32_t stage, F &&launch) {
+    int32_t armed = stage;
+    if (g_fail_stage.load(std::memory_order_relaxed) == stage &&
+        g_fail_stage.compare_exchange_strong(armed, PA_STAGE_NONE))
+        return PA_ERR_LAUNCH;
+    return launched(launch());
+}
+
 int64_t image_count(const pa_paged_args *a) {
     return (int64_t)a->num_reqs * tiles_per_request(a->max_ctx_len) * a->num_kv_heads;
 }
@@ -191,14 +204,14 @@ int run_attention(const pa_paged_args *a, int kind, AttnParams &p, const SplitOu
     const bool out_bf16 = out_dtype == PA_DTYPE_BF16;
     if (!so) {
         p.out = out;
-        return launched(launch_attention(kind, a->head_dim, out_bf16, p, a->max_q_len, stream));
+        return launch_stage(PA_STAGE_ATTENTION, [&] { return launch_attention(kind, a->head_dim, out_bf16, p, a->max_q_len, stream); });
     }
     p.sched = nullptr;   // split-KV items run in their plain XCD-contiguous order
     p.splits = so->n;
     p.o_part = so->o_part;
     p.lse_part = so->lse_part;
     p.out = nullptr;
-    int rc = launched(launch_attention(kind, a->head_dim, false, p, a->max_q_len, stream));
+    int rc = launch_stage(PA_STAGE_ATTENTION, [&] { return launch_attention(kind, a->head_dim, false, p, a->max_q_len, stream); });
     if (rc) return rc;
     MergeParams m{};
     m.cu_q = a->cu_q_lens;
@@ -214,7 +227,7 @@ int run_attention(const pa_paged_args *a, int kind, AttnParams &p, const SplitOu
     m.lse_part = so->lse_part;
     m.out = out;
     m.lse = so->lse;
-    return launched(launch_merge(m, out_bf16, a->max_q_len, stream));
+    return launch_stage(PA_STAGE_MERGE, [&] { return launch_merge(m, out_bf16, a->max_q_len, stream); });
 }
 
 int prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
@@ -230,10 +243,10 @@ int prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, cons
     ImageParams ip = image_params(a, workspace, KIND_BF16);
     ip.src = v_pool;
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
-    if (build && (rc = launched(launch_images(ip, IMG_BF16, false, stream)))) return rc;
+    if (build && (rc = launch_stage(PA_STAGE_IMAGES, [&] { return launch_images(ip, IMG_BF16, false, stream); }))) return rc;
     AttnParams p = attn_params(a);
     p.sched = so ? nullptr : schedule_ptr(a, PA_ENTRY_PREFILL_BF16, workspace);
-    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    if (build && p.sched && (rc = launch_stage(PA_STAGE_SCHEDULE, [&] { return launch_schedule(p, a->max_q_len, stream); }))) return rc;
     p.q = q;
     p.k = k_pool;
     p.v_img = (const char *)workspace;
@@ -259,10 +272,10 @@ int prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
     ip.src2 = k_pool;
     ip.src2_scales = k_scales;
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
-    if (build && (rc = launched(launch_images(ip, IMG_I8, true, stream)))) return rc;
+    if (build && (rc = launch_stage(PA_STAGE_IMAGES, [&] { return launch_images(ip, IMG_I8, true, stream); }))) return rc;
     AttnParams p = attn_params(a);
     p.sched = so ? nullptr : schedule_ptr(a, PA_ENTRY_PREFILL_INT8KV, workspace);
-    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    if (build && p.sched && (rc = launch_stage(PA_STAGE_SCHEDULE, [&] { return launch_schedule(p, a->max_q_len, stream); }))) return rc;
     p.q = q;
     p.v_img = (const char *)ip.dst;
     p.k_img = (const char *)ip.dst2;
@@ -320,18 +333,19 @@ int pa_prefill_fp8kv(const pa_paged_args *a, const void *q, const uint8_t *k_poo
     ip.src2 = k_pool;
     ip.fscale2 = k_scale;
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
-    if (build && (rc = launched(launch_images(ip, IMG_FP8, true, stream)))) return rc;
+    if (build && (rc = launch_stage(PA_STAGE_IMAGES, [&] { return launch_images(ip, IMG_FP8, true, stream); }))) return rc;
     AttnParams p = attn_params(a);
     p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_FP8KV, workspace);
-    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    if (build && p.sched && (rc = launch_stage(PA_STAGE_SCHEDULE, [&] { return launch_schedule(p, a->max_q_len, stream); }))) return rc;
     p.q = q;
     p.v_img = (const char *)ip.dst;
     p.k_img = (const char *)ip.dst2;
     p.img_tiles = ip.tiles;
     p.oscale = v_scale;   // the V image holds decoded values; the tensor scale multiplies O
     p.out = out;
-    return launched(launch_attention(KIND_I8KV, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
-                                     a->max_q_len, stream));
+    return launch_stage(PA_STAGE_ATTENTION, [&] {
+        return launch_attention(KIND_I8KV, a->head_dim, out_dtype == PA_DTYPE_BF16, p, a->max_q_len, stream);
+    });
 }
 
 int pa_k_stats(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
@@ -348,7 +362,7 @@ int pa_k_stats(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
     p.src_int8 = k_dtype == PA_DTYPE_INT8;
     p.src_scales = k_pool_scales;
     p.dst = ks;
-    return launched(launch_k_stats(p, stream));
+    return launch_stage(PA_STAGE_PASS, [&] { return launch_k_stats(p, stream); });
 }
 
 int pa_k_quant(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
@@ -367,7 +381,7 @@ int pa_k_quant(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
     p.src_scales = k_pool_scales;
     p.ks = ks;
     p.dst = k8;
-    return launched(launch_k_quant(p, stream));
+    return launch_stage(PA_STAGE_PASS, [&] { return launch_k_quant(p, stream); });
 }
 
 int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, const float *ks,
@@ -389,10 +403,10 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     ip.src = v_pool;
     ip.src_scales = v_scales;
     const bool build = !(a->flags & PA_FLAG_IMAGES_READY);
-    if (build && (rc = launched(launch_images(ip, v_dtype == PA_DTYPE_INT8 ? IMG_I8 : IMG_BF16, false, stream)))) return rc;
+    if (build && (rc = launch_stage(PA_STAGE_IMAGES, [&] { return launch_images(ip, v_dtype == PA_DTYPE_INT8 ? IMG_I8 : IMG_BF16, false, stream); }))) return rc;
     AttnParams p = attn_params(a);
     p.sched = schedule_ptr(a, PA_ENTRY_PREFILL_INT8QK, workspace);
-    if (build && p.sched && (rc = launched(launch_schedule(p, a->max_q_len, stream)))) return rc;
+    if (build && p.sched && (rc = launch_stage(PA_STAGE_SCHEDULE, [&] { return launch_schedule(p, a->max_q_len, stream); }))) return rc;
     p.cu_ctx = cu_ctx;
     p.q = q;
     p.k = k8;
@@ -400,8 +414,9 @@ int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, c
     p.v_img = (const char *)workspace;
     p.img_tiles = ip.tiles;
     p.out = out;
-    return launched(launch_attention(kind, a->head_dim, out_dtype == PA_DTYPE_BF16, p,
-                                     a->max_q_len, stream));
+    return launch_stage(PA_STAGE_ATTENTION, [&] {
+        return launch_attention(kind, a->head_dim, out_dtype == PA_DTYPE_BF16, p, a->max_q_len, stream);
+    });
 }
 
 size_t pa_workspace_bytes(const pa_paged_args *a, int32_t entry) {
@@ -434,7 +449,7 @@ int pa_fp8_dense_dequant(const pa_paged_args *a, const uint8_t *k_pool, const ui
     p.dst = k_scratch;
     p.dst2 = v_scratch;
     p.max_seq = max_seq;
-    return launched(launch_fp8_dequant(p, stream));
+    return launch_stage(PA_STAGE_PASS, [&] { return launch_fp8_dequant(p, stream); });
 }
 
 int pa_gather_kv(const pa_paged_args *a, const void *pool, int32_t elem_bytes,
@@ -449,7 +464,7 @@ int pa_gather_kv(const pa_paged_args *a, const void *pool, int32_t elem_bytes,
     p.src = pool;
     p.dst = dense;
     p.elem_bytes = elem_bytes;
-    return launched(launch_gather(p, stream));
+    return launch_stage(PA_STAGE_PASS, [&] { return launch_gather(p, stream); });
 }
 
 int pa_store_kv_int8(const pa_paged_args *a, const void *k_new, const void *v_new, int8_t *k_pool,
@@ -469,7 +484,7 @@ int pa_store_kv_int8(const pa_paged_args *a, const void *k_new, const void *v_ne
     p.dst2 = v_pool;
     p.dst_scales = k_scales;
     p.dst2_scales = v_scales;
-    return launched(launch_store_int8(p, stream));
+    return launch_stage(PA_STAGE_PASS, [&] { return launch_store_int8(p, stream); });
 }
 
 int pa_store_kv_fp8(const pa_paged_args *a, const void *k_new, const void *v_new,
@@ -489,7 +504,7 @@ int pa_store_kv_fp8(const pa_paged_args *a, const void *k_new, const void *v_new
     p.fscale2 = v_scale;
     p.dst = k_pool;
     p.dst2 = v_pool;
-    return launched(launch_store_fp8(p, stream));
+    return launch_stage(PA_STAGE_PASS, [&] { return launch_store_fp8(p, stream); });
 }
 
 int pa_peak_probe(int32_t dtype, int32_t workgroups, int32_t iters, float *out, hipStream_t stream) {
@@ -497,6 +512,12 @@ int pa_peak_probe(int32_t dtype, int32_t workgroups, int32_t iters, float *out, 
     if (!out) return PA_ERR_NULL;
     if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24)) return PA_ERR_SHAPE;
     return launched(launch_probe(dtype == PA_DTYPE_INT8, workgroups, iters, out, stream));
+}
+
+int pa_test_inject_failure(int32_t stage) {
+    if (stage < PA_STAGE_NONE || stage > PA_STAGE_PASS) return PA_ERR_SHAPE;
+    g_fail_stage.store(stage);
+    return PA_OK;
 }
 
 const char *pa_status_string(int32_t status) {

@@ -26,11 +26,13 @@ PA_FLAG_IMAGES_READY = 1
 PA_FLAG_APPEND = 2
 
 PA_MAX_SPLITS = 256
+PA_STAGE_NONE, PA_STAGE_IMAGES, PA_STAGE_SCHEDULE, PA_STAGE_ATTENTION = 0, 1, 2, 3
+PA_STAGE_MERGE, PA_STAGE_PASS = 4, 5
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
                 "pa_prefill_int8kv_splitkv", "pa_prefill_fp8kv", "pa_k_stats", "pa_k_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_store_kv_int8", "pa_store_kv_fp8",
-                "pa_gather_kv",
+                "pa_gather_kv", "pa_test_inject_failure",
                 "pa_peak_probe", "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
 
 
@@ -79,6 +81,7 @@ def lib():
             "pa_store_kv_int8": [pa, vp, vp, vp, vp, vp, vp, vp],
             "pa_store_kv_fp8": [pa, vp, vp, vp, vp, vp, vp, vp],
             "pa_peak_probe": [i32, i32, i32, vp, vp],
+            "pa_test_inject_failure": [i32],
         }
         for name, argt in sig.items():
             fn = getattr(L, name)
@@ -312,6 +315,12 @@ def pa_peak_probe(dtype: int, workgroups: int, iters: int, out, stream=None):
     _check(lib().pa_peak_probe(int(dtype), int(workgroups), int(iters), _p(out), _stream(stream)),
            "pa_peak_probe")
     return out
+
+
+def pa_test_inject_failure(stage: int):
+    """Test seam: the next launch of `stage` (PA_STAGE_*) fails without being
+    enqueued, and its call returns PA_ERR_LAUNCH; PA_STAGE_NONE disarms."""
+    _check(lib().pa_test_inject_failure(int(stage)), "pa_test_inject_failure")
 
 
 PROBE_FLOP_PER_MFMA = {PA_DTYPE_BF16: 32 * 32 * 16 * 2, PA_DTYPE_INT8: 32 * 32 * 32 * 2}

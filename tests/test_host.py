@@ -108,6 +108,31 @@ def test_entry_point_specific_errors():
     assert L.pa_peak_probe(ops.PA_DTYPE_INT8, 1, 1 << 25, p, None) == ops.PA_ERR_SHAPE
 
 
+def test_injected_failure_follows_argument_checks():
+    """pa_test_inject_failure: an armed stage turns the next call that reaches
+    it into PA_ERR_LAUNCH before that stage's launch (the image pass and the K
+    stats pass are the first launches of their calls, so nothing touches the
+    device here); argument errors still come first and leave it armed; it
+    fires once; unknown stages are refused."""
+    L = ops.lib()
+    a = _args()
+    p = C.c_void_p(4096)
+    big = 1 << 40
+    assert L.pa_test_inject_failure(6) == ops.PA_ERR_SHAPE
+    assert L.pa_test_inject_failure(-1) == ops.PA_ERR_SHAPE
+    try:
+        assert L.pa_test_inject_failure(ops.PA_STAGE_IMAGES) == ops.PA_OK
+        assert L.pa_prefill_bf16(C.byref(a), None, p, p, p, 0, p, big, None) == ops.PA_ERR_NULL
+        assert L.pa_prefill_bf16(C.byref(a), p, p, p, p, 0, p, big, None) == ops.PA_ERR_LAUNCH
+        assert L.pa_test_inject_failure(ops.PA_STAGE_PASS) == ops.PA_OK
+        assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_INT8, None, p, p, None) == ops.PA_ERR_NULL
+        assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_BF16, None, p, p, None) == ops.PA_ERR_LAUNCH
+        with pytest.raises(ops.PagedKVError):
+            ops.pa_test_inject_failure(9)
+    finally:
+        L.pa_test_inject_failure(ops.PA_STAGE_NONE)
+
+
 def test_split_kv_argument_errors():
     """Every call fails validation (split count, partial buffers, sizes) before
     anything is enqueued."""
