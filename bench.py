@@ -158,6 +158,34 @@ def measured_peaks(reps: int = 20):
     return res
 
 
+def measured_copy_gbs(nbytes: int = 1 << 31, reps: int = 10) -> float:
+    """The HBM rate a plain device-to-device copy reaches on this GPU (torch's
+    copy kernel over nbytes, read once and written once): the achievable
+    reference the HBM-bound passes are also reported against.  A measurement
+    aid only; no step of the path uses it."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    (ms,), _ = time_launches([lambda: dst.copy_(src)], reps, 2)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / ms * 1e-6
+
+
+def add_measured_hbm(arms: dict, gbs_peak: float):
+    """Beside every arm figure that has an HBM rate against the data-sheet
+    peak, the same rate against the measured copy rate."""
+    pairs = {"hbm_frac": ("gbs", "hbm_frac_of_measured"),
+             "dequant_hbm_frac": ("dequant_gbs", "dequant_hbm_frac_of_measured"),
+             "hbm_frac_images_ready": ("gbs_images_ready", "hbm_frac_of_measured_images_ready")}
+    for v in arms.values():
+        if isinstance(v, dict):
+            add_measured_hbm(v, gbs_peak)
+    for key, (gbs_key, out_key) in pairs.items():
+        if key in arms and gbs_key in arms:
+            arms[out_key] = arms[gbs_key] / gbs_peak
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, block_table, target_s: float = 12.0):
     """The oracle as it stands, on the host cores, over a sample of chunk rows
@@ -530,6 +558,9 @@ def main():
         progress("split-KV arms")
         arms.update(arm_store(args.steps, args.warmup))
         progress("store arms")
+        copy_gbs = measured_copy_gbs()
+        add_measured_hbm(arms, copy_gbs)
+        arms["measured_hbm_copy_gbs"] = copy_gbs
         line["arms"] = arms
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, top)
