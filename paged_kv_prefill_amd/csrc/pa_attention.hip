@@ -1008,10 +1008,17 @@ hipError_t launch_schedule(const AttnParams &p, int32_t max_q_len, hipStream_t s
 //     m = max_s lse_s,  w_s = e^{lse_s - m} (0 for an empty split),
 //     O = sum_s w_s O_s / sum_s w_s,  lse = m + ln sum_s w_s.
 constexpr int MERGE_THREADS = 256;
+#ifndef PA_MERGE_BATCH
+#define PA_MERGE_BATCH 32
+#endif
+constexpr int MERGE_BATCH = PA_MERGE_BATCH;   // splits whose partials are loaded together
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(const MergeParams P) {
     constexpr int PER = D / 64;
+    // one lane's PER consecutive fp32 of a partial row, as one load
+    using Vec = std::conditional_t<PER == 4, f32x4, std::conditional_t<PER == 2, f32x2, float>>;
+    static_assert(sizeof(Vec) == PER * sizeof(float), "merge vector");
     const int r = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t pair = (int64_t)blockIdx.x * (MERGE_THREADS / 64) + wave;   // row * Hq + head
@@ -1024,20 +1031,35 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(const MergeParams 
     if (pair >= (int64_t)Lq * P.Hq) return;
     const int64_t ph = (int64_t)q0 * P.Hq + pair;
     const float *ls = P.lse_part + ph * P.splits;
+    // the maximum: each lane takes every 64th split, then the wave's maximum
     float m = -INFINITY;
-    for (int s = 0; s < P.splits; ++s) m = fmaxf(m, ls[s]);
+    for (int s = lane; s < P.splits; s += 64) m = fmaxf(m, ls[s]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float wsum = 0.f;
-    for (int s = 0; s < P.splits; ++s) {
-        const float l = ls[s];
-        if (l == -INFINITY) continue;
-        const float w = expf(l - m);
-        wsum += w;
-        const float *o = P.o_part + (ph * P.splits + s) * D + lane * PER;
+    // the sums run over the splits in index order; MERGE_BATCH splits' loads are
+    // issued together before they are added
+    for (int s0 = 0; s0 < P.splits; s0 += MERGE_BATCH) {
+        float l[MERGE_BATCH];
+        float o[MERGE_BATCH][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * o[e];
+        for (int j = 0; j < MERGE_BATCH; ++j) {
+            const int s = s0 + j;
+            l[j] = s < P.splits ? ls[s] : -INFINITY;
+            const Vec v = *(const Vec *)(P.o_part + (ph * P.splits + (s < P.splits ? s : 0)) * D + lane * PER);
+            __builtin_memcpy(o[j], &v, sizeof(Vec));
+        }
+#pragma unroll
+        for (int j = 0; j < MERGE_BATCH; ++j) {
+            if (l[j] == -INFINITY) continue;   // an empty split (its partial is not written)
+            const float w = expf(l[j] - m);
+            wsum += w;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += w * o[j][e];
+        }
     }
     const float inv = 1.0f / wsum;
     if constexpr (OUT_BF16) {
