@@ -177,6 +177,9 @@ ImageParams image_params(const pa_paged_args *a, void *ws, int kind) {
     p.v_rpi = attn_rows_per_copy(kind, a->head_dim);
     p.dst2 = (char *)ws + image_count(a) * v_image_bytes(a->head_dim);
     p.cu_new = (a->flags & PA_FLAG_APPEND) ? a->cu_q_lens : nullptr;
+    // a chunk of at most max_q_len positions touches at most this many tiles
+    const int64_t touched = ((int64_t)a->max_q_len + TILE_KEYS - 1) / TILE_KEYS + 1;
+    p.new_tiles = touched < p.tiles ? touched : p.tiles;
     return p;
 }
 

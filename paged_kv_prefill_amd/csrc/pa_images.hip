@@ -52,9 +52,10 @@ __device__ __forceinline__ bool img_tile(const ImageParams &P, int &t, int &g, i
     if (L <= 0 || L > P.max_ctx || (int64_t)(L - 1) / P.block_size >= P.stride_bt) return false;
     if (P.cu_new) {   // append: tiles wholly before the chunk are already in place
         const int n = P.cu_new[r + 1] - P.cu_new[r];
-        if (n < 0 || n > L || t < (L - n) / TILE_KEYS) return false;
+        if (n < 0 || n > L) return false;
+        t += (L - n) / TILE_KEYS;   // the grid counts tiles from the chunk's first
     }
-    return t * TILE_KEYS < L;
+    return (int64_t)t * TILE_KEYS < L;
 }
 
 // e4m3fn codes -> fp32 with gfx950's converter (OCP E4M3)
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(IT) void k_image_kernel(const ImageParams P) {
 
 template <int D>
 static hipError_t launch_images_d(const ImageParams &p, int fmt, bool k_image, hipStream_t s) {
-    dim3 grid((uint32_t)p.tiles, (uint32_t)p.Hkv, (uint32_t)p.num_reqs);
+    dim3 grid((uint32_t)(p.cu_new ? p.new_tiles : p.tiles), (uint32_t)p.Hkv, (uint32_t)p.num_reqs);
     ImageParams pv = p;
     if (fmt == IMG_I8)
         hipLaunchKernelGGL((v_image_kernel<D, IMG_I8>), grid, dim3(IT), 0, s, pv);

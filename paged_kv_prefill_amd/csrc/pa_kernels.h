@@ -110,8 +110,10 @@ struct ImageParams {
     void *dst2;                 // K images
     const float *fscale2;       // fp8 pools: the K tensor's scale (device scalar)
     // append: only the tiles from the one holding each request's first chunk
-    // position on are rebuilt (cu_q: chunk prefix sums), the rest are kept
+    // position on are rebuilt (cu_q: chunk prefix sums), the rest are kept;
+    // the grid then spans new_tiles tiles per request, counted from that one
     const int32_t *cu_new;
+    int64_t new_tiles;
 };
 
 enum ImageSrc { IMG_BF16 = 0, IMG_I8 = 1, IMG_FP8 = 2 };   // pool element format of an image pass
