@@ -326,3 +326,31 @@ def test_peak_probe_runs(dtype):
     torch.cuda.synchronize()
     assert torch.isfinite(first).all().item()
     assert torch.equal(first, out)
+
+
+@pytest.mark.parametrize("arm", ["bf16", "int8kv", "int8qk", "fp8kv", "split_bf16", "split_int8kv"])
+def test_bf16_output_is_the_rounded_fp32_output(arm):
+    """Every arm's bf16 output is the fp32 output of the same call rounded to
+    bf16 (round half to even), bit for bit: the two outputs come from separate
+    kernel instantiations that must compute the same fp32 values."""
+    G = gc()
+    fmt = {"bf16": "bf16", "split_bf16": "bf16", "fp8kv": "fp8"}.get(arm, "int8")
+    w = synth.make_case(150, [37, 1, 130], [300, 9, 1000], 16, 8, 2, 128, kv_format=fmt)
+    case = G.DevCase(w)
+
+    def run(dt):
+        if arm == "bf16":
+            return case.run_bf16(out_dtype=dt)
+        if arm == "int8kv":
+            return case.run_int8kv(out_dtype=dt)
+        if arm == "int8qk":
+            return case.run_int8qk(out_dtype=dt)[0]
+        if arm == "fp8kv":
+            return case.run_fp8kv(out_dtype=dt)
+        return case.run_split(3, arm="bf16" if arm == "split_bf16" else "int8kv", out_dtype=dt)[0]
+
+    o32 = run(torch.float32)
+    o16 = run(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o32).all()
+    assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
