@@ -313,6 +313,37 @@ def test_work_schedule(shape):
         assert got <= 1.15 * ideal and got < 0.8 * base, (got, base, ideal)
 
 
+@pytest.mark.parametrize("shape", ["many_requests", "many_groups"])
+def test_work_schedule_fallback(orc, shape):
+    """Beyond 1,024 requests, or 1,024 (request, KV head) groups, the schedule
+    pass falls back to the plain XCD-contiguous layout: it must still list
+    every work item exactly once, and the outputs must match the oracle."""
+    from paged_kv_prefill_amd import ops
+    g = gc()
+    rng = np.random.default_rng(142)
+    if shape == "many_requests":
+        R, hq, hkv = 1100, 4, 1
+    else:
+        R, hq, hkv = 300, 8, 4
+    ctx = rng.integers(4, 41, R)
+    ql = np.minimum(rng.integers(1, 5, R), ctx)
+    w = synth.make_case(143, ql, ctx, 16, hq, hkv, 64)
+    assert R > 1024 or R * hkv > 1024
+    case = g.DevCase(w)
+    ws = ops.workspace(case.paged(), ops.PA_ENTRY_PREFILL_BF16)
+    out = case.out()
+    ops.pa_prefill_bf16(case.paged(), case.q, case.k_pool, case.v_pool, out, ws=ws)
+    torch.cuda.synchronize()
+    _, tiles = sched_items(w)
+    n = R * hkv * tiles
+    slots = -(-n // 8) * 8
+    off = sched_offset(w, "bf16")
+    sched = ws[off:off + 4 * slots].view(torch.int32).cpu().numpy()
+    assert sorted(sched[sched >= 0].tolist()) == list(range(n))
+    ref = g.oracle_rows(orc, w, synth.host_pools(w), None)
+    assert maxerr(out, ref) <= ATOL
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "int8"])
 def test_peak_probe_runs(dtype):
     """The MFMA probe (measurement export) runs, writes every output, finite,
