@@ -385,3 +385,61 @@ def test_bf16_output_is_the_rounded_fp32_output(arm):
     torch.cuda.synchronize()
     assert torch.isfinite(o32).all()
     assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+
+
+@pytest.mark.parametrize("bad", ["chunk_longer_than_context", "context_above_max", "context_beyond_table_row"])
+@pytest.mark.parametrize("arm", ["bf16", "split_bf16", "int8qk"])
+def test_inconsistent_request_is_skipped(orc, bad, arm):
+    """A request whose device lengths are inconsistent (chunk longer than its
+    context, context above max_ctx_len, context beyond what its block-table row
+    holds) is skipped: its output rows keep what they held, and the other
+    requests of the batch are computed as usual."""
+    from paged_kv_prefill_amd import ops
+    g = gc()
+    w = synth.make_case(160, [30, 20, 25], [100, 50, 80], 16, 8, 2, 64,
+                        kv_format="int8" if arm == "int8qk" else "bf16")
+    case = g.DevCase(w)
+    assert w.block_table.shape[1] == 7
+    ctx = w.ctx_lens.copy()
+    max_ctx = int(w.ctx_lens.max())
+    if bad == "chunk_longer_than_context":
+        ctx[1] = 19
+    elif bad == "context_above_max":
+        ctx[1] = max_ctx + 5
+    else:
+        max_ctx = 130
+        ctx[1] = 120            # needs 8 blocks, the row holds 7
+    p = ops.Paged(case.bts[0], case.cu_q, g.dev(ctx), int(w.q_lens.max()), max_ctx, w.block_size,
+                  w.num_blocks, w.num_q_heads, w.num_kv_heads, w.head_dim, w.softmax_scale)
+    out = case.out()
+    pools = synth.host_pools(w)
+    if arm == "bf16":
+        ops.pa_prefill_bf16(p, case.q, case.k_pool, case.v_pool, out)
+    elif arm == "split_bf16":
+        o_part, lse_part = ops.split_buffers(int(w.q_lens.sum()), w.num_q_heads, w.head_dim, 3, "cuda")
+        ops.pa_prefill_bf16_splitkv(p, case.q, case.k_pool, case.v_pool, out, 3, o_part, lse_part)
+    else:
+        total = int(w.ctx_lens.sum())
+        ks = torch.full((total, w.num_kv_heads), float("nan"), dtype=torch.float32, device="cuda")
+        k8 = torch.zeros((total, w.num_kv_heads, w.head_dim), dtype=torch.int8, device="cuda")
+        ops.pa_k_stats(p, case.k_pool, case.k_scales, case.cu_ctx, ks)
+        ops.pa_k_quant(p, case.k_pool, case.k_scales, case.cu_ctx, ks, k8)
+        ops.pa_prefill_int8qk(p, case.q, k8, ks, case.cu_ctx, case.v_pool, case.v_scales, out)
+    torch.cuda.synchronize()
+    cq = w.cu_q_lens
+    skipped = np.arange(cq[1], cq[2])
+    kept = np.concatenate([np.arange(cq[0], cq[1]), np.arange(cq[2], cq[3])]).astype(np.int32)
+    got = out.cpu().numpy()
+    assert np.isnan(got[skipped]).all(), "the skipped request's rows were written"
+    if arm == "int8qk":
+        ks_ref = orc.k_stats(w.block_table, w.ctx_lens, pools["k"], pools["k_scales"])
+        k8_ref = orc.k_quant(w.block_table, w.ctx_lens, pools["k"], ks_ref, pools["k_scales"])
+        cc = w.cu_ctx_lens
+        for r in (0, 2):
+            assert np.array_equal(ks.cpu().numpy()[cc[r]:cc[r + 1]].view(np.int32),
+                                  ks_ref[cc[r]:cc[r + 1]].view(np.int32))
+        ref = orc.prefill_int8qk(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, k8_ref, ks_ref,
+                                 pools["v"], w.softmax_scale, v_scales=pools["v_scales"], rows=kept)
+    else:
+        ref = g.oracle_rows(orc, w, pools, kept)
+    assert float(np.max(np.abs(got[kept].astype(np.float64) - ref))) <= ATOL
