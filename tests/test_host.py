@@ -268,3 +268,14 @@ def test_workload_recipes():
     used = np.concatenate([b.blocks_of(r) for r in range(b.num_reqs)])
     assert len(used) == len(set(used.tolist())) == 335
     assert np.mean(used > 2383) > 0.6 and int(used.max()) < 8000
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with a message that says so."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
