@@ -136,8 +136,15 @@ typedef struct pa_paged_args {
  *   k_pool   bf16 pool, v_pool bf16 pool (same strides)
  *   out      [sum Lq, Hq, D] of out_dtype (PA_DTYPE_F32 or PA_DTYPE_BF16)
  * QK^T on bf16 MFMA and PV on fp16 MFMA, both with fp32 accumulation; the
- * online softmax runs in fp32 and P is rounded to fp16 for PV.  V values must
- * stay below 65520 in magnitude (fp16 range); larger ones give inf/NaN rows.
+ * online softmax runs in fp32 and P is rounded to fp16 for PV.  V enters the
+ * PV MFMA as fp16 through its tile images: each 64-key tile is scaled by a
+ * power of two 2^-e (e >= 0, the smallest that brings the tile's largest |V|
+ * below 2^15; e = 0 for ordinary data) and the attention keeps its output
+ * accumulator in matching power-of-two units, so every finite bf16 V is
+ * served.  A bf16 value converts exactly unless its scaled magnitude falls
+ * below 2^-17, where fp16 is subnormal (spacing 2^-24): the error there is
+ * at most 2^-25 * 2^e.  NaN V values take no part in choosing e and reach
+ * the output as NaN; a tile that holds an infinite V is not scaled.
  */
 int pa_prefill_bf16(const pa_paged_args *args, const void *q, const void *k_pool,
                     const void *v_pool, void *out, int32_t out_dtype, void *workspace,
@@ -149,8 +156,13 @@ int pa_prefill_bf16(const pa_paged_args *args, const void *q, const void *k_pool
  * whose scale pointer is indexed by the same block id as the codes).
  *   k_pool, v_pool    int8 codes
  *   k_scales, v_scales fp32 [num_blocks, block_size, Hkv] (stride_sblock/stride_stok)
- * Each element is dequantised in the tile from code * scale (fp32), rounded
- * to bf16 for K and to fp16 for V, then the attention runs as pa_prefill_bf16.
+ * K: a per-token-head scale is constant along head_dim, so the codes
+ * themselves (exact in bf16) feed the bf16 QK^T MFMA and each key's fp32 scale
+ * multiplies its logit -- K is not rounded at all.  V: code * scale in fp32,
+ * rounded once to fp16 (times the tile's power-of-two range factor, as in
+ * pa_prefill_bf16) by the V image pass; fp16 P times fp16 V^T on the PV MFMA
+ * with fp32 accumulation.  A row that sees few keys therefore carries up to
+ * 2^-11 |V| of that rounding; over many keys it averages away.
  */
 int pa_prefill_int8kv(const pa_paged_args *args, const void *q, const int8_t *k_pool,
                       const int8_t *v_pool, const float *k_scales, const float *v_scales,
@@ -249,7 +261,11 @@ int pa_k_quant(const pa_paged_args *args, const void *k_pool, int32_t k_dtype,
  * pa_prefill_int8qk -- the int8-QK arm (HyperQwen PR #109, int8_qk=True): Q is
  * quantised per (token, q head) in the prologue (sq = max|q| / 127, codes
  * rounded half-even), S = float(int8 dot, int32 accumulate) * sq * ks * scale,
- * then fp32 online softmax and bf16 PV.
+ * then fp32 online softmax, P rounded to fp16, and fp16 P times fp16 V^T on
+ * the PV MFMA with fp32 accumulation (a bf16 V pool converts to fp16 exactly
+ * within its tile's range factor; an int8 V pool as code * scale rounded once
+ * to fp16, as in pa_prefill_int8kv).  A query row that is all zeros has scale
+ * 0 and codes 0: its logits are exactly 0.
  *   k8, ks     outputs of pa_k_quant / pa_k_stats, indexed by position
  *   v_pool     v_dtype PA_DTYPE_BF16 (bf16 pool) or PA_DTYPE_INT8 (codes, with v_scales)
  * PA_ERR_TOO_LARGE if max_ctx_len * num_kv_heads * head_dim >= 2^31 (one
@@ -263,8 +279,9 @@ int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8
 /*
  * pa_workspace_bytes -- device workspace an attention entry point needs for
  * these arguments: n = num_reqs * ceil(max_ctx_len / 64) * num_kv_heads V tile
- * images of 144 * head_dim + 256 bytes (fp16 rows of 64 keys padded to 72,
- * plus scales), and for PA_ENTRY_PREFILL_INT8KV / _FP8KV n more K tile images of
+ * images of 144 * head_dim + 256 bytes (fp16 rows of 64 keys padded to 72, the
+ * tile's power-of-two range factor in the padding of its first row, plus
+ * scales), and for PA_ENTRY_PREFILL_INT8KV / _FP8KV n more K tile images of
  * 128 * head_dim + 256 bytes; then, from the next multiple of 256 bytes, the
  * work schedule: 4 bytes per attention workgroup, num_reqs * num_kv_heads *
  * ceil(max_q_len * (num_q_heads / num_kv_heads) / 128) rounded up to a

@@ -18,10 +18,16 @@
 // 32 query columns held in registers for the whole loop), then O^T = V^T P^T
 // (A = 32 dims x 16 keys of V^T from LDS, B = P^T straight from the S
 // accumulators) with v_mfma_f32_32x32x16_f16: P lies in [0, 2^8], where fp16
-// keeps 11 significant bits against bf16's 8, and every bf16 V value of
-// magnitude below 65520 converts to fp16 exactly, so rounding P for the
-// matrix core costs 8x less accuracy than a bf16 P would.  (V of magnitude
-// 65520 or more overflows fp16 and shows as inf/NaN in the output.)
+// keeps 11 significant bits against bf16's 8, and a bf16 V value converts to
+// fp16 exactly (from 2^-17 up, where fp16 still holds its 8 significant bits),
+// so rounding P for the matrix core costs 8x less accuracy than a bf16 P
+// would.  V reaches fp16 through its tile image, scaled by a power of two 2^-e
+// per 64-key tile when its magnitudes would not fit (pa_layout.h); the
+// workgroup keeps O in units of 2^E, E the largest e it has met: a tile with a
+// larger e first rescales O (exactly, by a power of two), a tile with a
+// smaller one has its V rescaled in LDS before its PV, so P and the row sum
+// never change.  The prologue reads the factor of every tile in its key range
+// once; where all are 1 (ordinary data) the steps skip the factors entirely.
 // In the 32x32 accumulator layout lane l holds column l % 32, so every lane
 // owns one query column: the online softmax is lane-local except for one
 // exchange with the lane 32 away (v_permlane32_swap) per tile, and P never
@@ -114,8 +120,13 @@ struct AttnCfg {
     static constexpr int VSTAGE = V_BYTES;
     static constexpr int BT_OFF = 2 * KSTAGE + 2 * VSTAGE;
     // block-table entries cached in LDS by the FAST paged path
-    static constexpr int BT_CAP = K_PAGED ? ((LDS_MAX - BT_OFF) / 4 < 4096 ? (LDS_MAX - BT_OFF) / 4 : 4096) : 0;
-    static constexpr int LDS = BT_OFF + BT_CAP * 4;
+    static constexpr int BT_CAP =
+        K_PAGED ? ((LDS_MAX - BT_OFF - 16) / 4 < 4096 ? (LDS_MAX - BT_OFF - 16) / 4 : 4096) : 0;
+    // one word per wave: did its share of the V range factors hold one other than 1
+    // (inside the kernel's one LDS block: a second LDS object would hide from the
+    // compiler which LDS reads the direct-to-LDS copies can touch)
+    static constexpr int FLAG_OFF = BT_OFF + BT_CAP * 4;
+    static constexpr int LDS = FLAG_OFF + 4 * NWAVE;
     static constexpr int K_PER_WAVE = KCOPIES / NWAVE;
     static constexpr int V_PER_WAVE = (VCOPIES + NWAVE - 1) / NWAVE;
     static constexpr int KSTEPS = QK8 ? D / 32 : D / 16;
@@ -299,7 +310,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             }
             q8[ks] = i32x4{(int)wds[0], (int)wds[1], (int)wds[2], (int)wds[3]};
         }
-        lfac = sq * P.scale_log2;
+        // an all-zero query row (sq = 0) has all-zero codes, so its logits are
+        // exactly 0 whatever the factor: a factor of 0 would turn the masked
+        // logits' -inf into NaN in the exponent, so such a row takes sq = 1
+        lfac = (sq != 0.f ? sq : 1.f) * P.scale_log2;
     }
 
     // ---- block-table row of this request; the FAST paged path keeps it in LDS
@@ -425,6 +439,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 
     // ---- V^T tile kt (an image built by the V pass) into LDS stage `stage`
     auto v_src = [&](int kt) PA_INL { return rsrc_at(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D)); };
+
     auto v_copy = [&](__amdgpu_buffer_rsrc_t img, int stage, int i) PA_INL {
         char *vl = vstage(stage);
         const int q = i * NWAVE + wave_u;
@@ -513,11 +528,14 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
     // logit -> log2 units, applied by the softmax's own multiply-add: the int8-QK
-    // logits stay int dot * key scale until then, and an all-zero query row (sq
-    // = 0, so lfac = 0) gives zero logits, never 0 * inf
+    // logits stay int dot * key scale until then.  The factor is never 0 (see
+    // the Q quantisation), so a masked logit's -inf stays -inf
     const float smfac = lfac;
     float m_run = -INFINITY;   // running (lazy) max of the log2-domain logits
     float l_run = 0.f;         // this half-wave's share of the running sum
+    // O's units 2^E as fp32 bits (see the V range factor in pa_layout.h): the
+    // same on every wave, which all meet the same tiles in the same order
+    uint32_t vcur = 0x3f800000u;
 
     // causal / context mask of tile kt's logits (tiles that reach past the
     // workgroup's first column only)
@@ -558,6 +576,40 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             m_run = m_new;
         }
     };
+    // a V tile whose range factor vf (2^e, fp32 bits) differs from O's units:
+    // a larger one moves O to the new units, a smaller one moves this tile's V
+    // (in LDS stage `stage`, every wave a quarter of its rows) to O's, with a
+    // barrier before anyone reads it.  Both factors are powers of two, so
+    // nothing is rounded unless it leaves the range of its format.
+    auto v_range = [&](uint32_t vf, int stage) PA_INL {
+        if (vf > vcur) {
+            const float f = __uint_as_float(vcur) / __uint_as_float(vf);
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                asm volatile("" : "+a"(o[db]));
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= f;
+                asm volatile("" : "+a"(o[db]));
+            }
+            vcur = vf;
+        } else {
+            const float f = __uint_as_float(vf) / __uint_as_float(vcur);
+            char *vt = vstage(stage);
+            // one chunk at a time: a rare path, kept out of the loop's registers
+#pragma unroll 1
+            for (int i = 0; i < D / 32; ++i) {
+                const int c = lane + 64 * i;   // 16-byte chunk of this wave's D / 4 rows
+                f16x8 *pv = (f16x8 *)(vt + (wave_u * (D / 4) + c / 8) * VT_ROW_BYTES + (c % 8) * 16);
+                f16x8 v = *pv;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = (_Float16)((float)v[j] * f);
+                *pv = v;
+            }
+            __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+            barrier_lds();
+        }
+    };
+
     // ---- main loop, software-pipelined by one tile: step kt turns tile kt's
     // logits into P and adds P V(kt) into O while the QK MFMAs of tile kt+1
     // run, so the softmax's vector work overlaps matrix-core work.  K runs one
@@ -565,10 +617,24 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // copies of K(kt+2) and V(kt+1) stream into the other stages.
     // Tiles are numbered absolutely; stage parity counts from kt_begin.
     f32x16 sa[2], sb[2];
+    // does any V tile of this workgroup's key range carry a range factor other
+    // than 1 (a scaled tile)?  One factor word per tile, read by the threads in
+    // turn; the answer is the workgroup's and decides, once, whether the steps
+    // look at the factors at all
     dma_k(kt_begin, 0);
     dma_v(kt_begin, 0);
     dma_k(min(kt_begin + 1, kt_end - 1), 1);
+    bool scaled = false;   // (read while the first tiles' copies are in flight)
+    for (int kt = kt_begin + tid; kt < kt_end; kt += NTHR)
+        scaled |= *(const uint32_t *)(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D) +
+                                      VT_FACTOR_OFF) != 0x3f800000u;
+    uint32_t *flags = (uint32_t *)(smem + C::FLAG_OFF);
+    const bool wave_scaled = __any(scaled);
+    if (lane == 0) flags[wave] = wave_scaled ? 1u : 0u;
     __syncthreads();
+    const u32x4 fl = *(const u32x4 *)flags;
+    const bool vr_any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]) != 0;
+    static_assert(NWAVE == 4, "one flag word per wave, read as one 16-byte vector");
     qk_tile(0, sa);
     if (kt_begin >= t_mask) mask_tile(sa, kt_begin);
     float mx = tile_max(sa);
@@ -637,6 +703,12 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         u32x4 ka[NQ];
         f16x8 va[NP];
         f32x4 ksc[2][4];
+        // V(kt)'s range factor, before any read of its operands (only where
+        // some tile of this workgroup's range is scaled)
+        if (__builtin_expect(vr_any, 0)) {
+            const uint32_t vf = __builtin_amdgcn_readfirstlane(*(const uint32_t *)(vl + VT_FACTOR_OFF));
+            if (vf != vcur) v_range(vf, cur);
+        }
 #pragma unroll
         for (int n = 0; n < PFV; ++n) va[n] = rdV(vr, n);
         if constexpr (NEXT) {
@@ -792,7 +864,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // ---- epilogue: O / l, row of this lane's column; a split-KV partial also
     // records its range's log-sum-exp, ln(sum_j e^{s_j}) = ln2 (m_run + log2 l)
     const float l_tot = sum_halves(l_run);
-    const float inv = (P.oscale ? *P.oscale : 1.0f) / l_tot;
+    const float inv = (P.oscale ? *P.oscale : 1.0f) * __uint_as_float(vcur) / l_tot;
     if (!col_valid) return;
     int64_t orow = ((int64_t)(q0 + tok) * P.Hq + h) * D;
     float *out_f32 = (float *)P.out;

@@ -65,68 +65,82 @@ __device__ __forceinline__ float fp8_at(uint32_t word, int b) {
     return (b >> 1) ? hi[b & 1] : lo[b & 1];
 }
 
-// V^T image: [D][72] fp16 (64 columns in MFMA-position order + zero padding)
-// + 64 scales in position order.  One unit = 4 consecutive positions (4
-// consecutive columns) x one 16-byte chunk of the source row; its 4 x 8 (bf16)
-// or 4 x 16 (int8, fp8) values go to LDS as 8-byte groups of the 4 columns of
-// one dim.
+// V^T image: [D][72] fp16 (64 columns in MFMA-position order + zero padding,
+// the tile's range factor 2^e in row 0's padding) + 64 scales in position
+// order.  One unit = 4 consecutive positions (4 consecutive columns) x one
+// 16-byte chunk of the source row; its 4 x 8 (bf16) or 4 x 16 (int8, fp8)
+// values go to LDS as 8-byte groups of the 4 columns of one dim.  The values
+// are read first (all of a thread's units), the tile's largest magnitude is
+// reduced over the workgroup, and then they are scaled by 2^-e (exact) and
+// rounded once to fp16.
 template <int D, int SRC>
 __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
     constexpr bool SRC_I8 = SRC != IMG_BF16;   // one byte per element
     constexpr int CPR = (SRC_I8 ? D : 2 * D) / 16;
+    constexpr int EPC = SRC_I8 ? 16 : 8;       // values per 16-byte chunk
     constexpr int UNITS = 16 * CPR;
+    constexpr int NU = (UNITS + IT - 1) / IT;  // units per thread
     constexpr int V_BYTES = vt_tile_bytes(D);
     __shared__ __attribute__((aligned(16))) char img[V_BYTES + TILE_KEYS * 4];
+    __shared__ float wave_amax[IT / 64];
     int t, g, r, L;
     if (!img_tile(P, t, g, r, L)) return;
     const int tid = threadIdx.x;
     const int rpi = P.v_rpi;
     float *scl = (float *)(img + V_BYTES);
     for (int d = tid; d < D; d += IT) *(u32x4 *)(img + d * VT_ROW_BYTES + TILE_KEYS * 2) = u32x4{0, 0, 0, 0};
-    for (int u = tid; u < UNITS; u += IT) {
+    float x[NU][4][EPC];
+    float amax = 0.f;
+#pragma unroll
+    for (int ui = 0; ui < NU; ++ui) {
+        const int u = tid + ui * IT;
         const int dc = u % CPR, pg = u / CPR;
-        u32x4 w[4];
-        float s[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = t * TILE_KEYS + tile_key(pg * 4 + j, rpi);
             int64_t off = 0, soff = 0;
-            const bool ok = key < L && img_row(P, r, key, g, off, soff);
+            const bool ok = u < UNITS && key < L && img_row(P, r, key, g, off, soff);
+            u32x4 w;
+            float s = 0.f;
             if (SRC_I8) {
-                w[j] = ok ? *(const u32x4 *)((const int8_t *)P.src + off + dc * 16) : u32x4{0, 0, 0, 0};
-                s[j] = ok ? (SRC == IMG_FP8 ? 1.0f : P.src_scales[soff]) : 0.f;
+                w = ok ? *(const u32x4 *)((const int8_t *)P.src + off + dc * 16) : u32x4{0, 0, 0, 0};
+                s = ok ? (SRC == IMG_FP8 ? 1.0f : P.src_scales[soff]) : 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    x[ui][j][e] = (SRC == IMG_FP8 ? fp8_at(w[e >> 2], e & 3)
+                                                  : (float)(int8_t)((w[e >> 2] >> ((e & 3) * 8)) & 0xff)) * s;
             } else {
-                w[j] = ok ? *(const u32x4 *)((const __bf16 *)P.src + off + dc * 8) : u32x4{0, 0, 0, 0};
-                s[j] = 0.f;
+                w = ok ? *(const u32x4 *)((const __bf16 *)P.src + off + dc * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[ui][j][e] = (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]);
             }
-        }
-        const int slot = vt_slot(pg * 4);
-        if (SRC_I8) {
+            if (u < UNITS && dc == 0) scl[pg * 4 + j] = s;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float x[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    x[j] = (SRC == IMG_FP8 ? fp8_at(w[j][e >> 2], e & 3)
-                                           : (float)(int8_t)((w[j][e >> 2] >> ((e & 3) * 8)) & 0xff)) * s[j];
-                *(u32x2 *)(img + vt_off(dc * 16 + e, slot)) =
-                    u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = (e & 1) ? bf16hi(w[j][e >> 1]) : bf16lo(w[j][e >> 1]);
-                *(u32x2 *)(img + vt_off(dc * 8 + e, slot)) =
-                    u32x2{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3])};
-            }
-        }
-        if (dc == 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) scl[pg * 4 + j] = s[j];
+            for (int e = 0; e < EPC; ++e) amax = fmaxf(amax, fabsf(x[ui][j][e]));
         }
     }
+    // the tile's largest magnitude: over the wave, then over the waves
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    if ((tid & 63) == 0) wave_amax[tid >> 6] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < IT / 64; ++w) amax = fmaxf(amax, wave_amax[w]);
+    const int e_range = vt_range_exp(__float_as_uint(amax));
+    const float down = __uint_as_float((uint32_t)(127 - e_range) << 23);   // 2^-e, exact
+#pragma unroll
+    for (int ui = 0; ui < NU; ++ui) {
+        const int u = tid + ui * IT;
+        if (u >= UNITS) continue;
+        const int dc = u % CPR, pg = u / CPR;
+        const int slot = vt_slot(pg * 4);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+            *(u32x2 *)(img + vt_off(dc * EPC + e, slot)) =
+                u32x2{pack_f16x2(x[ui][0][e] * down, x[ui][1][e] * down),
+                      pack_f16x2(x[ui][2][e] * down, x[ui][3][e] * down)};
+    }
+    if (tid == 0) *(float *)(img + VT_FACTOR_OFF) = __uint_as_float((uint32_t)(127 + e_range) << 23);
     __syncthreads();
     char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * v_image_bytes(D);
     constexpr int CHUNKS = (V_BYTES + TILE_KEYS * 4) / 16;

@@ -19,6 +19,14 @@
 // columns 8-15: the order in which the S accumulator rows reach the PV MFMA,
 // so each PV operand is one 16-byte read.
 //
+// fp16 tops out at 65504, so a tile holds V * 2^-e: e >= 0 is the smallest
+// power of two that brings the tile's largest |V| below 2^15 (0 for any tile
+// whose values are all below 2^15 in magnitude, or that holds an infinity;
+// NaNs take no part in the maximum).
+// The factor 2^e itself, as an fp32, sits in the padding of row 0 (byte
+// VT_FACTOR_OFF), which the PV operands never read, so it reaches LDS with the
+// tile's own copies.
+//
 // V^T images in global memory (the workspace) are byte-for-byte copies of the
 // LDS tile followed by 64 fp32 per-key scales in position order (int8 V), so
 // a workgroup moves them with straight 1 KB direct-to-LDS copies.  K images
@@ -33,6 +41,16 @@ constexpr int TILE_KEYS = 64;
 constexpr int VT_ROW_BYTES = TILE_KEYS * 2 + 16;   // one padded V^T row (fp16)
 
 constexpr int K_COPY_STRIDE = 1024 + 16;          // LDS bytes per 1 KB K copy
+constexpr int VT_FACTOR_OFF = TILE_KEYS * 2;      // fp32 2^e of a V^T tile: row 0's padding
+constexpr int VT_RANGE_LOG2 = 15;                 // a tile's |V| * 2^-e stays below 2^15
+
+// e of a V^T tile whose largest magnitude is amax (see above): from amax's
+// exponent field, amax < 2^(field - 126); 0 for an infinite amax
+__host__ __device__ inline int vt_range_exp(uint32_t amax_bits) {
+    const int field = (int)((amax_bits >> 23) & 0xff);
+    const int e = field - 126 - VT_RANGE_LOG2;
+    return (field == 0xff || e < 0) ? 0 : e;
+}
 
 // key (0..63) held at MFMA position p = 32 * kb + i of a K tile whose rows are
 // copied rpi at a time (rpi in {2, 4, 8, 16})
