@@ -280,6 +280,24 @@ def store_kv_int8(block_table, ctx_lens, cu_new, k_new, v_new, k_pool, v_pool, k
         raise ValueError(f"oracle_store_kv_int8 failed ({rc})")
 
 
+def quantise_int8(k_new, v_new, lib=None):
+    """Dense rows [n, Hkv, D] of bf16 K and V -> (k codes, k scales, v codes,
+    v scales) in the int8 per-token-head format, by the quantise-on-store
+    writer above: the n rows are stored as one request's whole context in a
+    one-block pool of block_size n, whose block is then the dense result."""
+    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+    v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+    n, hkv, d = k_new.shape
+    assert v_new.shape == k_new.shape and n >= 1
+    k8 = np.zeros((1, n, hkv, d), dtype=np.int8)
+    v8 = np.zeros_like(k8)
+    ks = np.full((1, n, hkv), np.nan, dtype=np.float32)
+    vs = np.full_like(ks, np.nan)
+    store_kv_int8(np.zeros((1, 1), np.int32), np.array([n], np.int32),
+                  np.array([0, n], np.int32), k_new, v_new, k8, v8, ks, vs, lib=lib)
+    return k8[0], ks[0], v8[0], vs[0]
+
+
 def store_kv_fp8(block_table, ctx_lens, cu_new, k_new, v_new, k_scale, v_scale, k_pool, v_pool,
                  lib=None):
     """Quantise-on-store into host fp8 e4m3fn pools (in place)."""

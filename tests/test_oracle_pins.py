@@ -40,6 +40,12 @@ def dense_values(w, which):
     raise ValueError(w.kv_format)
 
 
+def q8(orc, w):
+    """An int8 workload's codes and scales, from its bf16 sources by the
+    oracle's quantise-on-store writer."""
+    return w.quantised(orc.quantise_int8) if w.int8_sources else w
+
+
 def run_oracle(orc, w, pools=None, rows=None, causal=True, lib=None):
     pools = pools if pools is not None else synth.host_pools(w)
     return orc.prefill(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
@@ -157,7 +163,7 @@ def test_empty_chunks_match_masked_sdpa(orc):
 
 @pytest.mark.parametrize("fmt", ["int8", "fp8"])
 def test_scaled_pools_require_their_scales(orc, fmt):
-    w = synth.make_case(8, [3], [9], 4, 2, 1, 64, kv_format=fmt)
+    w = q8(orc, synth.make_case(8, [3], [9], 4, 2, 1, 64, kv_format=fmt))
     pools = synth.host_pools(w)
     with pytest.raises(ValueError):
         orc.prefill(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
@@ -180,7 +186,7 @@ def test_noncausal_matches_sdpa(orc):
 
 
 def test_int8_kv_matches_sdpa_on_dequantised_values(orc):
-    w = synth.make_case(8, [6, 4], [19, 8], 5, 4, 2, 64, kv_format="int8")
+    w = q8(orc, synth.make_case(8, [6, 4], [19, 8], 5, 4, 2, 64, kv_format="int8"))
     ours = run_oracle(orc, w)
     ref = sdpa_reference(w)
     assert np.max(np.abs(ours - ref)) < 1e-12
@@ -367,7 +373,7 @@ def test_placement_invariance_with_poisoned_pool(orc):
 
 def test_gather_round_trip(orc):
     for fmt in ("bf16", "int8", "fp8"):
-        w = synth.make_case(14, [3, 5], [21, 30], 7, 4, 2, 64, kv_format=fmt, num_blocks=30)
+        w = q8(orc, synth.make_case(14, [3, 5], [21, 30], 7, 4, 2, 64, kv_format=fmt, num_blocks=30))
         pools = synth.host_pools(w)
         assert np.array_equal(orc.gather_kv(w.block_table, w.ctx_lens, pools["k"]), w.k)
         assert np.array_equal(orc.gather_kv(w.block_table, w.ctx_lens, pools["v"]), w.v)
@@ -452,11 +458,30 @@ def test_k_quant_invariants_bf16_source(orc):
     assert np.all(err <= ks[..., None].astype(np.float64) * (0.5 + 1e-5))
 
 
+def test_quantise_int8_dense_equals_k_passes(orc):
+    """The dense int8 quantiser (the writer storing n rows as one request's
+    whole context in a one-block pool) gives, for every row of a bf16
+    workload, exactly the K-stats scale and the K-quant codes of the same
+    values read from their paged pool -- for K and, by symmetry, for V."""
+    w = synth.make_case(31, [3, 5], [37, 20], 8, 4, 2, 64, num_blocks=20)
+    pools = synth.host_pools(w)
+    k8, ks, v8, vs = orc.quantise_int8(w.k, w.v)
+    for codes, scales, name in ((k8, ks, "k"), (v8, vs, "v")):
+        s_ref = orc.k_stats(w.block_table, w.ctx_lens, pools[name])
+        c_ref = orc.k_quant(w.block_table, w.ctx_lens, pools[name], s_ref)
+        assert np.array_equal(scales.view(np.int32), s_ref.view(np.int32))
+        assert np.array_equal(codes, c_ref)
+    assert np.all(np.abs(k8).max(axis=2) == 127)
+    wq = w.with_block_table(w.block_table)
+    wq.kv_format = "int8"
+    assert wq.int8_sources and not q8(orc, wq).int8_sources
+
+
 def test_k_quant_of_int8_pool_keeps_codes(orc):
     """Re-quantising an absmax/127 int8 row reproduces its codes exactly (the
     fp32 round trip moves x/s by far less than half a code) and its scale to
     within one ulp."""
-    w = synth.make_case(16, [5], [45], 8, 4, 2, 64, kv_format="int8", num_blocks=12)
+    w = q8(orc, synth.make_case(16, [5], [45], 8, 4, 2, 64, kv_format="int8", num_blocks=12))
     pools = synth.host_pools(w)
     ks = orc.k_stats(w.block_table, w.ctx_lens, pools["k"], pools["k_scales"])
     k8 = orc.k_quant(w.block_table, w.ctx_lens, pools["k"], ks, pools["k_scales"])
