@@ -20,8 +20,8 @@ launch time, against the bf16 dense MFMA peak, and also against the MFMA
 throughput the chip sustains on the same instruction shape with no other work
 (pa_peak_probe, measured in the same run); timed with the image pass
 skipped via PA_FLAG_IMAGES_READY), its HBM bytes per launch from the committed
-counter profile when that was taken on this build, the CPU oracle's rate on a
-bounded sample, and the other arms (the headline with a bf16 output, int8 KV
+counter profile when that was taken on this build, the CPU oracle's rate over
+the same 2,048-row chunk, and the other arms (the headline with a bf16 output, int8 KV
 exact-QK, int8-QK with its two K passes, fp8 KV through the dense bf16 scratch, the batched 8-request chunk,
 split-KV on a short chunk and on a spec-decode verify at 60,000 context, the
 quantise-on-store writers) measured per call.
@@ -96,8 +96,18 @@ class Pools:
             self.v = torch.zeros(shape, dtype=torch.int8, device=DEV)
             self.k_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
             self.v_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
-            synth.fill_pool(wp, self.k, dev(w.k), self.k_scales, dev(w.k_scales))
-            synth.fill_pool(wp, self.v, dev(w.v), self.v_scales, dev(w.v_scales))
+            if w.int8_sources:
+                # the N(0,1) bf16 values stored as int8 per-token-head codes by the
+                # library's quantise-on-store writer (every context position)
+                mc = int(w.ctx_lens.max())
+                whole = ops.Paged(self.bt, self.cu_ctx, self.ctx, mc, mc, w.block_size, w.num_blocks,
+                                  w.num_q_heads, w.num_kv_heads, w.head_dim, w.softmax_scale)
+                ops.pa_store_kv_int8(whole, dev_bf16(w.k), dev_bf16(w.v), self.k, self.v,
+                                     self.k_scales, self.v_scales)
+                torch.cuda.synchronize()
+            else:
+                synth.fill_pool(wp, self.k, dev(w.k), self.k_scales, dev(w.k_scales))
+                synth.fill_pool(wp, self.v, dev(w.v), self.v_scales, dev(w.v_scales))
         else:
             self.k = torch.full(shape, synth.FP8_NAN, dtype=torch.uint8, device=DEV)
             self.v = torch.full(shape, synth.FP8_NAN, dtype=torch.uint8, device=DEV)
@@ -206,26 +216,37 @@ def add_measured_hbm(arms: dict, gbs_peak: float):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(w, block_table, target_s: float = 12.0):
-    """The oracle as it stands, on the host cores, over a sample of chunk rows
-    (all q heads) spread over the chunk; tokens/s of the sample."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(w, block_table):
+    """The oracle as it stands, on the host cores, over exactly the chunk the
+    GPU times: all 2,048 rows, all 16 q heads, each against its ~20,000 keys;
+    tokens/s of that chunk."""
     from oracle import oracle as orc
     pools = synth.host_pools(w.with_block_table(block_table), poison_all=False)
     threads = len(os.sched_getaffinity(0))
     lib = orc.load()
-    n = 8
-    while True:
-        rows = np.linspace(0, int(w.q_lens[0]) - 1, n).astype(np.int32)
-        t0 = time.perf_counter()
-        orc.prefill(block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
-                    w.softmax_scale, rows=rows, threads=threads, lib=lib)
-        dt = time.perf_counter() - t0
-        if dt >= target_s / 3 or n >= int(w.q_lens[0]):
-            break
-        n = min(int(w.q_lens[0]), max(n * 2, int(n * target_s / max(dt, 1e-3))))
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of the 2,048 chunk rows (all 16 q heads, ~20k keys each), "
-                      f"fp64 oracle, {dt:.1f} s wall"}
+    n = int(w.q_lens[0])
+    rows = np.arange(n, dtype=np.int32)
+    t0 = time.perf_counter()
+    orc.prefill(block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
+                w.softmax_scale, rows=rows, threads=threads, lib=lib)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": f"the whole timed chunk: all {n} rows (all 16 q heads, 17,953-20,000 keys "
+                      f"each), fp64 oracle on {threads} threads, {dt:.1f} s wall"}
 
 
 # ------------------------------------------------------------------ arms

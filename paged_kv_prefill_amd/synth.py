@@ -15,7 +15,12 @@ fp8 KV served in 2,048-token chunks over a 32k context).
 
 Storage conventions (all host numpy arrays):
   bf16   -> np.uint16 bit patterns
-  int8   -> np.int8 codes plus one np.float32 scale per (token, KV head)
+  int8   -> drawn as N(0,1) bf16 source values (np.uint16 bits); the int8 codes
+            and per-(token, KV head) scales are what a quantise-on-store writer
+            makes of them.  This module does not quantise: a consumer turns the
+            sources into codes with its own writer (`Workload.quantised`), so
+            the test side uses the oracle's and the GPU side the library's,
+            and the two pools are compared bit for bit.
   fp8    -> np.uint8 e4m3fn codes plus one np.float32 scale per tensor
 Pools are [num_blocks, block_size, num_kv_heads, head_dim]; Q and O are
 [sum of chunk lengths, num_q_heads, head_dim]; dense K/V are
@@ -52,21 +57,6 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
 
 
-def int8_per_token_head(rng: np.random.Generator, n_tok: int, n_heads: int, d: int):
-    """Codes and scales in the int8_per_token_head format: every (token, head)
-    row holds one code of magnitude 127 (so its scale is the row's absmax / 127)
-    and other codes from a rounded normal of spread ~42 (clipped to +-126).
-    Scales are drawn directly, in the range that absmax/127 of 256 standard
-    normal values falls in.  No quantisation is performed here."""
-    codes = np.clip(np.rint(rng.standard_normal((n_tok, n_heads, d), dtype=np.float32) * 42.0),
-                    -126, 126).astype(np.int8)
-    where = rng.integers(0, d, size=(n_tok, n_heads))
-    sign = np.where(rng.integers(0, 2, size=(n_tok, n_heads)) == 0, -127, 127).astype(np.int8)
-    np.put_along_axis(codes, where[..., None], sign[..., None], axis=2)
-    scales = rng.uniform(2.4 / 127.0, 3.6 / 127.0, size=(n_tok, n_heads)).astype(np.float32)
-    return codes, scales
-
-
 def fp8_per_tensor(rng: np.random.Generator, shape):
     """N(0,1) float32 values stored as e4m3fn codes with one fp32 scale per
     tensor.  The scale is drawn from [0.014, 0.02] so that every value / scale
@@ -94,14 +84,35 @@ class Workload:
     q: np.ndarray                     # uint16 bf16 bits [sum q, Hq, D]
     k: np.ndarray                     # dense K by position [sum ctx, Hkv, D]
     v: np.ndarray
-    k_scales: Optional[np.ndarray] = None   # int8: float32 [sum ctx, Hkv]
-    v_scales: Optional[np.ndarray] = None
+    k_scales: Optional[np.ndarray] = None   # int8: float32 [sum ctx, Hkv] (None: k/v are
+    v_scales: Optional[np.ndarray] = None   #   still the bf16 sources, see `quantised`)
     k_scale: Optional[np.float32] = None    # fp8: per-tensor scale
     v_scale: Optional[np.float32] = None
     causal: bool = True
     extra: dict = field(default_factory=dict)
 
     # -- derived sizes -----------------------------------------------------
+    @property
+    def int8_sources(self) -> bool:
+        """An int8 workload whose k / v still hold the bf16 source values."""
+        return self.kv_format == "int8" and self.k_scales is None
+
+    def quantised(self, quantise) -> "Workload":
+        """The same workload with its int8 codes and scales, made by
+        `quantise(k_bf16, v_bf16) -> (k_codes, k_scales, v_codes, v_scales)`
+        (dense [sum ctx, Hkv, D] bf16 bits in; int8 codes and float32
+        [sum ctx, Hkv] scales out) from the bf16 sources.  The source values
+        stay available as extra['k_src'] / extra['v_src']."""
+        assert self.int8_sources, "not an int8 workload with bf16 sources"
+        k8, ks, v8, vs = quantise(self.k, self.v)
+        w = Workload(**{**self.__dict__})
+        w.extra = {**self.extra, "k_src": self.k, "v_src": self.v}
+        w.k, w.v = np.ascontiguousarray(k8, np.int8), np.ascontiguousarray(v8, np.int8)
+        w.k_scales = np.ascontiguousarray(ks, np.float32)
+        w.v_scales = np.ascontiguousarray(vs, np.float32)
+        assert w.k.shape == self.k.shape and w.k_scales.shape == self.k.shape[:2]
+        return w
+
     @property
     def num_reqs(self) -> int:
         return int(len(self.q_lens))
@@ -171,6 +182,8 @@ def host_pools(w: Workload, poison_all: bool = True):
     """Host K/V pools (and int8 scale pools).  With poison_all the whole pool is
     written with poison; otherwise the pool is lazily zero-allocated and only
     the tail slots of each request's last block are poisoned (large pools)."""
+    if w.int8_sources:
+        raise ValueError("int8 workload not quantised yet (Workload.quantised)")
     shape = w.pool_shape
     dt = w.kv_np_dtype
     out = {}
@@ -201,8 +214,10 @@ def make_case(seed: int, q_lens, ctx_lens, block_size: int, num_q_heads: int,
               num_kv_heads: int, head_dim: int, kv_format: str = "bf16",
               num_blocks: Optional[int] = None, placement: str = "random",
               causal: bool = True, name: str = "case") -> Workload:
-    """A small seeded workload.  Draw order: block table, then per request K
-    then V (and their scales), then Q for all chunks, then the fp8 scales."""
+    """A small seeded workload.  Draw order: block table, then K then V (all
+    requests; fp8 draws each tensor's scale after its values), then Q for all
+    chunks.  int8 workloads draw exactly the bf16 values of the same seed, as
+    sources for a quantise-on-store writer."""
     rng = np.random.default_rng(seed)
     q_lens = np.asarray(q_lens, dtype=np.int32)
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
@@ -229,12 +244,9 @@ def make_case(seed: int, q_lens, ctx_lens, block_size: int, num_q_heads: int,
     total = int(ctx_lens.sum())
     ks = vs = None
     kscale = vscale = None
-    if kv_format == "bf16":
+    if kv_format in ("bf16", "int8"):
         k = normal_bf16(rng, (total, num_kv_heads, head_dim))
         v = normal_bf16(rng, (total, num_kv_heads, head_dim))
-    elif kv_format == "int8":
-        k, ks = int8_per_token_head(rng, total, num_kv_heads, head_dim)
-        v, vs = int8_per_token_head(rng, total, num_kv_heads, head_dim)
     elif kv_format == "fp8":
         k, kscale = fp8_per_tensor(rng, (total, num_kv_heads, head_dim))
         v, vscale = fp8_per_tensor(rng, (total, num_kv_heads, head_dim))
@@ -289,17 +301,13 @@ def config_bigpool_bf16() -> Workload:
 
 
 def config_bigpool_int8() -> Workload:
-    """Same shape and placements as the bf16 big-pool case, K/V stored as int8
-    with one fp32 scale per token per KV head."""
-    rng = np.random.default_rng(2)
-    k, ks = int8_per_token_head(rng, BIGPOOL_L, BIG_HKV, BIG_D)
-    v, vs = int8_per_token_head(rng, BIGPOOL_L, BIG_HKV, BIG_D)
-    q = normal_bf16(rng, (CHUNK, BIG_HQ, BIG_D))
-    bottom, top = _bigpool_tables()
-    w = Workload("bigpool_int8", "int8", np.array([CHUNK], np.int32),
-                 np.array([BIGPOOL_L], np.int32), BIG_BS, BIGPOOL_BLOCKS,
-                 BIG_HQ, BIG_HKV, BIG_D, bottom, q, k, v, ks, vs)
-    w.extra["top_block_table"] = top
+    """Same shape, placements and source values as the bf16 big-pool case (seed
+    1), with K/V kept as int8 codes and one fp32 absmax / 127 scale per token
+    per KV head: the bf16 values are returned as the sources a quantise-on-store
+    writer turns into that pool (`Workload.quantised`)."""
+    w = config_bigpool_bf16()
+    w.name = "bigpool_int8"
+    w.kv_format = "int8"
     return w
 
 
@@ -365,19 +373,16 @@ VERIFY_Q = 8
 def config_verify(kv_format: str = "int8") -> Workload:
     """Spec-decode verify: one request whose last 8 tokens (the drafted ones)
     attend to a 60,000-token context; block 880, 4 KV / 16 q heads, head_dim
-    256, 2,600-block pool.  K/V bf16 (seed 6) or int8 with one fp32 scale per
-    token per KV head (seed 7).  Returned at the top placement (blocks
+    256, 2,600-block pool.  K/V bf16 N(0,1) (seed 6), or int8 with one fp32
+    scale per token per KV head, drawn as N(0,1) bf16 sources (seed 7) for a
+    quantise-on-store writer.  Returned at the top placement (blocks
     2,532..2,599); `bottom_block_table` holds blocks 0..68."""
+    if kv_format not in ("bf16", "int8"):
+        raise ValueError(kv_format)
     rng = np.random.default_rng(6 if kv_format == "bf16" else 7)
     ks = vs = None
-    if kv_format == "bf16":
-        k = normal_bf16(rng, (VERIFY_L, BIG_HKV, BIG_D))
-        v = normal_bf16(rng, (VERIFY_L, BIG_HKV, BIG_D))
-    elif kv_format == "int8":
-        k, ks = int8_per_token_head(rng, VERIFY_L, BIG_HKV, BIG_D)
-        v, vs = int8_per_token_head(rng, VERIFY_L, BIG_HKV, BIG_D)
-    else:
-        raise ValueError(kv_format)
+    k = normal_bf16(rng, (VERIFY_L, BIG_HKV, BIG_D))
+    v = normal_bf16(rng, (VERIFY_L, BIG_HKV, BIG_D))
     q = normal_bf16(rng, (VERIFY_Q, BIG_HQ, BIG_D))
     nb = -(-VERIFY_L // BIG_BS)                                      # 69 blocks
     top = np.arange(BIGPOOL_BLOCKS - nb, BIGPOOL_BLOCKS, dtype=np.int32)[None, :]

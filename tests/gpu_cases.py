@@ -1,6 +1,12 @@
 """Device-side construction of seeded workloads for the GPU parity tests, and
 the matching host pools for the oracle.  Plumbing only: torch is used for
-device memory and copies; every computation goes through the C ABI."""
+device memory and copies; every computation goes through the C ABI.
+
+int8 workloads arrive as N(0,1) bf16 sources.  The device pools are written
+from them by the library's quantise-on-store writer (pa_store_kv_int8), the
+host pools by the oracle's (`host_workload`), and `check_int8_pools` asserts
+the two are the same bytes: the GPU side never feeds the oracle and the
+oracle never feeds the GPU."""
 from __future__ import annotations
 
 import numpy as np
@@ -48,6 +54,19 @@ class DevCase:
             self.v_pool = torch.zeros(shape, dtype=torch.int8, device=DEV)
             self.k_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
             self.v_scales = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+            if w.int8_sources:
+                # quantise-on-store of every context position, at every placement
+                ks_src, vs_src = dev_bf16(w.k), dev_bf16(w.v)
+                for bt in self.tables:
+                    p = ops.Paged(dev(bt), self.cu_ctx, self.ctx, int(w.ctx_lens.max()),
+                                  int(w.ctx_lens.max()), w.block_size, w.num_blocks,
+                                  w.num_q_heads, w.num_kv_heads, w.head_dim, w.softmax_scale)
+                    ops.pa_store_kv_int8(p, ks_src, vs_src, self.k_pool, self.v_pool,
+                                         self.k_scales, self.v_scales)
+                torch.cuda.synchronize()
+                del ks_src, vs_src
+                self.bts = [dev(t) for t in self.tables]
+                return
             kd, vd = dev(w.k), dev(w.v)
             kds, vds = dev(w.k_scales), dev(w.v_scales)
         elif w.kv_format == "fp8":
@@ -153,6 +172,60 @@ class DevCase:
                             device=DEV)
         ops.pa_gather_kv(self.paged(which), pool, self.cu_ctx, dense)
         return dense
+
+
+def host_workload(w: synth.Workload, orc) -> synth.Workload:
+    """The workload as the oracle sees it: int8 sources quantised by the
+    oracle's own quantise-on-store writer; other formats unchanged."""
+    return w.quantised(orc.quantise_int8) if w.int8_sources else w
+
+
+def check_int8_pools(case: "DevCase", wq: synth.Workload):
+    """The device int8 pools (codes and scales) that the library's writer
+    filled equal the oracle writer's, bit for bit, over every block the
+    workload uses at every placement, tail slots included."""
+    for which, bt in enumerate(case.tables):
+        wp = wq.with_block_table(bt)
+        host = synth.host_pools(wp, poison_all=False)
+        blocks = np.unique(np.concatenate([wp.blocks_of(r) for r in range(wp.num_reqs)]))
+        idx = torch.from_numpy(blocks.astype(np.int64)).to(DEV)
+        for name, pool in (("k", case.k_pool), ("v", case.v_pool)):
+            got = pool.index_select(0, idx).cpu().numpy()
+            assert np.array_equal(got, host[name][blocks]), f"{name} codes differ (table {which})"
+        for name, pool in (("k_scales", case.k_scales), ("v_scales", case.v_scales)):
+            got = pool.index_select(0, idx).cpu().numpy().view(np.int32)
+            assert np.array_equal(got, host[name][blocks].view(np.int32)), \
+                f"{name} differ (table {which})"
+
+
+# fp16 keeps 11 significant bits: rounding a normal value x to fp16 moves it
+# by at most 2^-11 |x|
+F16_REL = 2.0 ** -11
+
+
+def v_rounding_bound(orc, wq: synth.Workload, pools, rows=None, block_table=None):
+    """The part of the error that rounding V to fp16 contributes, elementwise:
+    every int8 arm takes V_j = code * scale rounded once to fp16, so output
+    element (i, h, d) moves by at most 2^-11 sum_j w_ij |V_jd|, where w_ij are
+    the row's softmax weights -- the oracle's attention over |V|, which is the
+    pool with every code replaced by its magnitude.  A row with one visible key
+    carries the whole 2^-11 |V_0d|; rows over many keys average it away."""
+    absv = dict(pools)
+    absv["v"] = np.abs(pools["v"]).astype(np.int8)
+    return F16_REL * oracle_rows(orc, wq, absv, rows, block_table)
+
+
+def gate(gpu_out: torch.Tensor, ref: np.ndarray, atol: float, extra=None, rows=None):
+    """max |gpu - ref| over the (listed) rows, and whether every element is
+    within atol (+ the elementwise `extra` bound where given); non-finite GPU
+    output fails."""
+    g = gpu_out.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        g = g[rows]
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    d = np.abs(g - ref)
+    lim = atol if extra is None else atol + extra
+    return float(d.max()), bool(np.all(d <= lim))
 
 
 def host_pools_multi(w: synth.Workload, tables, poison_all: bool):

@@ -100,6 +100,6 @@ def test_pass_failure(orc):
     assert torch.isnan(ks).all()
     out, ks2, _ = case.run_int8qk()
     torch.cuda.synchronize()
-    pools = synth.host_pools(w)
+    pools = synth.host_pools(G.host_workload(w, orc))
     ks_ref = orc.k_stats(w.block_table, w.ctx_lens, pools["k"], pools.get("k_scales"))
     assert np.array_equal(ks2.cpu().numpy().view(np.int32), ks_ref.view(np.int32))

@@ -39,6 +39,9 @@ def test_long_context_small_blocks(orc, fmt):
     w = synth.make_case(140, [LQ], [L], BS, 16, 4, 256, kv_format=fmt)
     assert -(-L // BS) > 4096, "the block-table row exceeds the kernel's LDS cache"
     case = G.DevCase(w)
+    w = G.host_workload(w, orc)
+    if fmt == "int8":
+        G.check_int8_pools(case, w)
     pools = synth.host_pools(w)
     rows = _rows(w)
     ref = G.oracle_rows(orc, w, pools, rows)

@@ -158,16 +158,23 @@ def test_one_split_is_the_plain_kernel(c):
 
 @pytest.mark.parametrize("c", [CASES[2], CASES[3]], ids=["s203", "s204"])
 def test_split_int8kv_matches_oracle(orc, c):
+    """int8 pools written by the library's writer from N(0,1) values (equal to
+    the oracle writer's); the merged output is gated at 1e-3 plus the bound
+    that V's fp16 rounding contributes (rows with few keys carry it whole)."""
     G = gc()
     w = make(c, "int8")
     case = G.DevCase(w)
-    ref, ref_lse = oracle_lse(orc, w, synth.host_pools(w))
+    wq = G.host_workload(w, orc)
+    G.check_int8_pools(case, wq)
+    pools = synth.host_pools(wq)
+    ref, ref_lse = oracle_lse(orc, wq, pools)
+    vb = G.v_rounding_bound(orc, wq, pools)
     for splits in (1, 7):
         out, lse, _, _ = case.run_split(splits, arm="int8kv")
-        err = float(np.max(np.abs(np64(out) - ref)))
+        err, ok = G.gate(out, ref, ATOL, vb)
         lerr = float(np.max(np.abs(np64(lse) - ref_lse)))
         print(f"{c[0]} int8kv splits {splits}: out err {err:.3g}, lse err {lerr:.3g}", flush=True)
-        assert err <= ATOL and lerr <= LSE_ATOL
+        assert ok and lerr <= LSE_ATOL
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "int8"])
@@ -188,8 +195,11 @@ def test_verify_60k(orc, fmt):
     assert np.array_equal(bits(lse_top), bits(lse_bot))
     out_again, lse_again, _, _ = case.run_split(splits, arm=arm, which=0)
     assert np.array_equal(bits(out_again), bits(out_top)) and np.array_equal(bits(lse_again), bits(lse_top))
-    pools = synth.host_pools(w, poison_all=False)
-    ref, ref_lse = oracle_lse(orc, w, pools)
+    wq = G.host_workload(w, orc)
+    if fmt == "int8":
+        G.check_int8_pools(case, wq)
+    pools = synth.host_pools(wq, poison_all=False)
+    ref, ref_lse = oracle_lse(orc, wq, pools)
     err = float(np.max(np.abs(np64(out_top) - ref)))
     lerr = float(np.max(np.abs(np64(lse_top) - ref_lse)))
     print(f"verify {fmt}: out err {err:.3g}, lse err {lerr:.3g}", flush=True)
