@@ -151,6 +151,29 @@ int pa_prefill_bf16(const pa_paged_args *args, const void *q, const void *k_pool
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_prefill_bf16_noalloc -- pa_prefill_bf16 for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops that must not
+ * call the allocator, harnesses that forbid it.  Same arguments, checks,
+ * kernels and results as pa_prefill_bf16, without the workspace: the call's
+ * tile images and work schedule go to a device array of
+ * PA_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held from the
+ * library's first use on that GPU until the process ends, found with the GPU
+ * current).  The call allocates nothing.
+ *   - Calls on one GPU share that array: calls that overlap on it (other
+ *     streams, other host threads) race.  Nothing in it needs clearing.
+ *   - PA_ERR_TOO_LARGE if pa_workspace_bytes(args, PA_ENTRY_PREFILL_BF16)
+ *     exceeds PA_NOALLOC_SCRATCH_BYTES (e.g. one request of head_dim 256 and 4
+ *     KV heads up to a context of 28,864 tokens); nothing is enqueued.
+ *   - PA_ERR_SHAPE if args->flags is not 0 (no call may rely on what an
+ *     earlier one left in the shared array).
+ *   - PA_ERR_LAUNCH if the array's device address cannot be found.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int pa_prefill_bf16_noalloc(const pa_paged_args *args, const void *q, const void *k_pool,
+                            const void *v_pool, void *out, int32_t out_dtype,
+                            hipStream_t stream);
+
+/*
  * pa_prefill_int8kv -- the exact-QK arm over an int8 per-token-head pool
  * (HyperQwen PR #91, first comment and merge review: int8_per_token_head KV,
  * whose scale pointer is indexed by the same block id as the codes).

@@ -233,6 +233,21 @@ int run_attention(const pa_paged_args *a, int kind, AttnParams &p, const SplitOu
     return launch_stage(PA_STAGE_MERGE, [&] { return launch_merge(m, out_bf16, a->max_q_len, stream); });
 }
 
+}  // namespace
+
+// the argument checks of pa_prefill_bf16 that precede its workspace check
+int pa::prefill_bf16_check(const pa_paged_args *a, const void *q, const void *k_pool,
+                           const void *v_pool, void *out, int32_t out_dtype) {
+    int rc = check_common(a, 2, true);
+    if (rc) return rc;
+    if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (!k_pool || !v_pool) return PA_ERR_NULL;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+namespace {
+
 int prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
                  const SplitOut *so, void *out, int32_t out_dtype, void *workspace,
                  size_t workspace_bytes, hipStream_t stream) {
@@ -240,8 +255,7 @@ int prefill_bf16(const pa_paged_args *a, const void *q, const void *k_pool, cons
     if (rc) return rc;
     if ((rc = check_out(q, out, out_dtype))) return rc;
     if (so && (rc = check_split(a, *so))) return rc;
-    if (!k_pool || !v_pool) return PA_ERR_NULL;
-    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    if ((rc = pa::prefill_bf16_check(a, q, k_pool, v_pool, out, out_dtype))) return rc;
     if ((rc = check_workspace(a, PA_ENTRY_PREFILL_BF16, workspace, workspace_bytes))) return rc;
     ImageParams ip = image_params(a, workspace, KIND_BF16);
     ip.src = v_pool;

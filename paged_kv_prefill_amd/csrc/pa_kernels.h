@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct pa_paged_args;   // include/paged_kv_prefill.h
+
 namespace pa {
 
 struct FastDivHost {
@@ -135,6 +137,11 @@ hipError_t launch_gather(const PassParams &p, hipStream_t stream);
 hipError_t launch_store_int8(const PassParams &p, hipStream_t stream);
 hipError_t launch_store_fp8(const PassParams &p, hipStream_t stream);
 hipError_t launch_probe(bool int8, int32_t workgroups, int32_t iters, float *out, hipStream_t stream);
+
+// host side of the ABI, shared by its source files: pa_prefill_bf16's argument
+// checks short of the workspace (status code; no HIP call)
+int prefill_bf16_check(const ::pa_paged_args *a, const void *q, const void *k_pool,
+                       const void *v_pool, void *out, int32_t out_dtype);
 
 constexpr int ATTN_THREADS = 256;
 constexpr int ATTN_COLS = 128;   // (token, q head) columns per workgroup

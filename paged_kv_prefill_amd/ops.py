@@ -29,7 +29,7 @@ PA_MAX_SPLITS = 256
 PA_STAGE_NONE, PA_STAGE_IMAGES, PA_STAGE_SCHEDULE, PA_STAGE_ATTENTION = 0, 1, 2, 3
 PA_STAGE_MERGE, PA_STAGE_PASS = 4, 5
 
-ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
+ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_bf16_noalloc", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
                 "pa_prefill_int8kv_splitkv", "pa_prefill_fp8kv", "pa_k_stats", "pa_k_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_store_kv_int8", "pa_store_kv_fp8",
                 "pa_gather_kv", "pa_test_inject_failure",
@@ -69,6 +69,7 @@ def lib():
         vp, i32, sz, pa = C.c_void_p, C.c_int32, C.c_size_t, C.POINTER(PagedArgs)
         sig = {
             "pa_prefill_bf16": [pa, vp, vp, vp, vp, i32, vp, sz, vp],
+            "pa_prefill_bf16_noalloc": [pa, vp, vp, vp, vp, i32, vp],
             "pa_prefill_int8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
             "pa_prefill_bf16_splitkv": [pa, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
             "pa_prefill_fp8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
@@ -195,6 +196,19 @@ def pa_prefill_bf16(p: Paged, q, k_pool, v_pool, out, ws=None, stream=None):
     ws, wp, wn = _ws(p, PA_ENTRY_PREFILL_BF16, ws)
     _check(lib().pa_prefill_bf16(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(out), dt, wp, wn,
                                  _stream(stream)), "pa_prefill_bf16")
+    return out
+
+
+PA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def pa_prefill_bf16_noalloc(p: Paged, q, k_pool, v_pool, out, stream=None):
+    """pa_prefill_bf16 without a workspace: the library's own per-GPU array
+    holds the images and schedule (calls on one GPU must not overlap)."""
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    _check(lib().pa_prefill_bf16_noalloc(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(out), dt,
+                                         _stream(stream)), "pa_prefill_bf16_noalloc")
     return out
 
 

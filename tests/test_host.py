@@ -108,6 +108,28 @@ def test_entry_point_specific_errors():
     assert L.pa_peak_probe(ops.PA_DTYPE_INT8, 1, 1 << 25, p, None) == ops.PA_ERR_SHAPE
 
 
+def test_noalloc_argument_errors():
+    """pa_prefill_bf16_noalloc: pa_prefill_bf16's argument errors, then flags
+    refused and workspaces beyond its array refused, all before any HIP call."""
+    L = ops.lib()
+    p = C.c_void_p(4096)
+    a = _args()
+    assert L.pa_prefill_bf16_noalloc(None, p, p, p, p, 0, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16_noalloc(C.byref(a), None, p, p, p, 0, None) == ops.PA_ERR_NULL
+    assert L.pa_prefill_bf16_noalloc(C.byref(a), p, p, p, p, 7, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_prefill_bf16_noalloc(C.byref(_args(num_q_heads=3)), p, p, p, p, 0, None) == ops.PA_ERR_SHAPE
+    assert L.pa_prefill_bf16_noalloc(C.byref(_args(flags=ops.PA_FLAG_IMAGES_READY)), p, p, p, p, 0,
+                                     None) == ops.PA_ERR_SHAPE
+    # the largest context of one request (head_dim 256, 4 KV heads, chunk 2,048)
+    # whose workspace fits the array, and the next 64-key tile
+    geo = dict(head_dim=256, num_kv_heads=4, num_q_heads=16, stride_head=256, stride_tok=1024,
+               block_size=880, stride_block=880 * 1024, stride_bt=40, max_q_len=2048)
+    fits, over = _args(max_ctx_len=28864, **geo), _args(max_ctx_len=28865, **geo)
+    assert L.pa_workspace_bytes(C.byref(fits), ops.PA_ENTRY_PREFILL_BF16) <= ops.PA_NOALLOC_SCRATCH_BYTES
+    assert L.pa_workspace_bytes(C.byref(over), ops.PA_ENTRY_PREFILL_BF16) > ops.PA_NOALLOC_SCRATCH_BYTES
+    assert L.pa_prefill_bf16_noalloc(C.byref(over), p, p, p, p, 0, None) == ops.PA_ERR_TOO_LARGE
+
+
 def test_injected_failure_follows_argument_checks():
     """pa_test_inject_failure: an armed stage turns the next call that reaches
     it into PA_ERR_LAUNCH before that stage's launch (the image pass and the K
