@@ -22,7 +22,8 @@ throughput the chip sustains on the same instruction shape with no other work
 skipped via PA_FLAG_IMAGES_READY), its HBM bytes per launch from the committed
 counter profile when that was taken on this build, the CPU oracle's rate over
 the same 2,048-row chunk, and the other arms (the headline with a bf16 output, int8 KV
-exact-QK, int8-QK with its two K passes, fp8 KV through the dense bf16 scratch, the batched 8-request chunk,
+exact-QK, int8-QK with its fused K pass (and the two separate passes), fp8 KV through the dense
+bf16 scratch, the batched 8-request chunk,
 split-KV on a short chunk and on a spec-decode verify at 60,000 context, the
 quantise-on-store writers) measured per call.
 """
@@ -338,22 +339,28 @@ def arm_int8(steps, warmup, peaks=None):
     exact = lambda: ops.pa_prefill_int8kv(p, P.q, P.k, P.v, P.k_scales, P.v_scales, out, ws_e)
     stats = lambda: ops.pa_k_stats(p, P.k, P.k_scales, P.cu_ctx, ks)
     quant = lambda: ops.pa_k_quant(p, P.k, P.k_scales, P.cu_ctx, ks, k8)
+    fused = lambda: ops.pa_k_stats_quant(p, P.k, P.k_scales, P.cu_ctx, ks, k8)
     qk8 = lambda: ops.pa_prefill_int8qk(p, P.q, k8, ks, P.cu_ctx, P.v, P.v_scales, out, ws_q)
     (t_exact,), _ = time_launches([exact], steps, warmup)
-    (t_stats, t_quant, t_qk8), _ = time_launches([stats, quant, qk8], steps, warmup)
+    (t_fused, t_qk8), _ = time_launches([fused, qk8], steps, warmup)
+    (t_stats, t_quant), _ = time_launches([stats, quant], steps, warmup)
     fl = attn_flops(w)
     elems = total * w.num_kv_heads * w.head_dim
     rows = total * w.num_kv_heads
     stats_bytes = elems + rows * 4 + rows * 4
     quant_bytes = elems + rows * 4 + rows * 4 + elems
+    fused_bytes = elems + rows * 4 + elems + rows * 4     # codes + scales read, k8 + ks written
     blended = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
     chunk = int(w.q_lens.sum())
     return {
         "int8kv_exact_qk": {"ms": t_exact, "tokens_per_s": chunk / t_exact * 1e3,
                             "tflops": fl / t_exact * 1e-9,
                             "mfma_frac": fl / t_exact * 1e-9 / PEAK_BF16_TFLOPS},
-        "int8_qk": {"ms_total": t_stats + t_quant + t_qk8, "ms_attention": t_qk8,
-                    "tokens_per_s": chunk / (t_stats + t_quant + t_qk8) * 1e3,
+        "int8_qk": {"ms_total": t_fused + t_qk8, "ms_attention": t_qk8,
+                    "tokens_per_s": chunk / (t_fused + t_qk8) * 1e3,
+                    "k_stats_quant": {"ms": t_fused, "gbs": fused_bytes / t_fused * 1e-6,
+                                      "hbm_frac": fused_bytes / t_fused * 1e-6 / PEAK_HBM_GBS},
+                    "ms_total_separate_passes": t_stats + t_quant + t_qk8,
                     "attention_tops": fl / t_qk8 * 1e-9,
                     "mfma_frac_blended_peak": fl / t_qk8 * 1e-9 / blended,
                     **({"mfma_frac_blended_measured": fl / t_qk8 * 1e-9 /

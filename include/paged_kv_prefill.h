@@ -281,6 +281,18 @@ int pa_k_quant(const pa_paged_args *args, const void *k_pool, int32_t k_dtype,
                int8_t *k8, hipStream_t stream);
 
 /*
+ * pa_k_stats_quant -- pa_k_stats and pa_k_quant in one pass over K (HyperQwen
+ * PR #109: the stats and quant kernels of the int8 prefill, both reading K
+ * through the block table): each (token, KV head) row of K is read once and
+ * gives both its scale and its codes.  ks and k8 are exactly what pa_k_stats
+ * followed by pa_k_quant write, bit for bit; arguments, layouts and errors as
+ * theirs.
+ */
+int pa_k_stats_quant(const pa_paged_args *args, const void *k_pool, int32_t k_dtype,
+                     const float *k_pool_scales, const int32_t *cu_ctx, float *ks, int8_t *k8,
+                     hipStream_t stream);
+
+/*
  * pa_prefill_int8qk -- the int8-QK arm (HyperQwen PR #109, int8_qk=True): Q is
  * quantised per (token, q head) in the prologue (sq = max|q| / 127, codes
  * rounded half-even), S = float(int8 dot, int32 accumulate) * sq * ks * scale,

@@ -401,6 +401,25 @@ int pa_k_quant(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
     return launch_stage(PA_STAGE_PASS, [&] { return launch_k_quant(p, stream); });
 }
 
+int pa_k_stats_quant(const pa_paged_args *a, const void *k_pool, int32_t k_dtype,
+                     const float *k_pool_scales, const int32_t *cu_ctx, float *ks, int8_t *k8,
+                     hipStream_t stream) {
+    if (k_dtype != PA_DTYPE_BF16 && k_dtype != PA_DTYPE_INT8) return PA_ERR_UNSUPPORTED;
+    int rc = check_common(a, k_dtype == PA_DTYPE_INT8 ? 1 : 2, false);
+    if (rc) return rc;
+    if (!k_pool || !cu_ctx || !ks || !k8) return PA_ERR_NULL;
+    if (k_dtype == PA_DTYPE_INT8 && (rc = check_scales(a, k_pool_scales))) return rc;
+    if (!aligned16(k_pool) || !aligned16(k8)) return PA_ERR_SHAPE;
+    PassParams p = pass_params(a);
+    p.cu_ctx = cu_ctx;
+    p.src = k_pool;
+    p.src_int8 = k_dtype == PA_DTYPE_INT8;
+    p.src_scales = k_pool_scales;
+    p.dst = ks;
+    p.dst2 = k8;
+    return launch_stage(PA_STAGE_PASS, [&] { return launch_k_stats_quant(p, stream); });
+}
+
 int pa_prefill_int8qk(const pa_paged_args *a, const void *q, const int8_t *k8, const float *ks,
                       const int32_t *cu_ctx, const void *v_pool, int32_t v_dtype,
                       const float *v_scales, void *out, int32_t out_dtype, void *workspace,

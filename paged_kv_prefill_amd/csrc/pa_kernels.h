@@ -132,6 +132,8 @@ hipError_t launch_images(const ImageParams &p, int fmt, bool k_image, hipStream_
 hipError_t launch_schedule(const AttnParams &p, int32_t max_q_len, hipStream_t stream);
 hipError_t launch_k_stats(const PassParams &p, hipStream_t stream);
 hipError_t launch_k_quant(const PassParams &p, hipStream_t stream);
+// K stats and K quant in one pass: ks into dst, k8 into dst2
+hipError_t launch_k_stats_quant(const PassParams &p, hipStream_t stream);
 hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t stream);
 hipError_t launch_gather(const PassParams &p, hipStream_t stream);
 hipError_t launch_store_int8(const PassParams &p, hipStream_t stream);

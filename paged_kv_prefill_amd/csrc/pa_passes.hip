@@ -4,6 +4,7 @@
 //            ks[t, g] = max_d |K[t, g, d]| / 127, fp32
 //   K quant  (same PR, the quant kernel writing int8 K by position):
 //            k8[t, g, d] = clamp(rne(K / ks), -127, 127), 0 where ks == 0
+//   both in one pass over K (the two results of the two kernels, bit for bit)
 //   fp8 dense dequant (vllm.cpp PR #3360, "What changed"):
 //            scratch[r, t, g, d] = bf16_rne(fp32(e4m3fn(code)) * scale)
 //   gather   (test export): dense[t, g, :] = pool row (t, g)
@@ -43,74 +44,152 @@ __device__ __forceinline__ bool request_ok(const PassParams &P, int r, int &L) {
     return L > 0 && L <= P.max_ctx && (int64_t)(L - 1) / P.block_size < P.stride_bt;
 }
 
-// fp32 values of one 16-byte source chunk (8 from bf16, 16 from int8 codes * scale)
-__device__ __forceinline__ int chunk_values(const PassParams &P, int64_t off, int64_t soff,
-                                            int sub, bool ok, float *x) {
-    if (P.src_int8) {
-        u32x4 w = ok ? *(const u32x4 *)((const int8_t *)P.src + off + sub * 16) : u32x4{0, 0, 0, 0};
-        const float s = ok ? P.src_scales[soff] : 0.f;
+// Codes clamp(rne(x / s), -127, 127) (0 where s == 0) of n values, exactly as
+// with an IEEE division per value but without one: r = 1 / s is the row's one
+// correctly rounded reciprocal, and q = x * r lies within 2^-16 of x / s when
+// |x / s| <= 127.5 (two roundings of at most 2^-24 each; s = amax / 127 keeps
+// |x / s| below that, and beyond it both sides clamp to +-127), so when every
+// q of the chunk is farther than 2^-15 from a half-integer, x / s rounds to
+// q's nearest integer.  A chunk with a q that is not (rare), or whose
+// reciprocal is not finite (s == 0 or subnormal), takes the divisions.
+// Non-finite values need no care: an inf / NaN q rounds to the code the
+// division gives (NaN clamps to -127 on both sides).
+template <int N>
+__device__ __forceinline__ void quant_codes(const float *x, float s, uint32_t *packed) {
+    const float r = 1.0f / s;
+    float y[N], dev = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = (float)(int8_t)((w[e >> 2] >> ((e & 3) * 8)) & 0xff) * s;
-        return 16;
+    for (int e = 0; e < N; ++e) {
+        const float q = x[e] * r;
+        y[e] = rintf(q);
+        dev = fmaxf(dev, fabsf(q - y[e]));   // a NaN difference (inf / NaN q) is skipped
     }
-    u32x4 w = ok ? *(const u32x4 *)((const __bf16 *)P.src + off + sub * 8) : u32x4{0, 0, 0, 0};
+    if (__builtin_expect(!(dev <= 0.5f - 0x1p-15f) || !(fabsf(r) <= 3.4028234663852886e38f), 0)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]);
-    return 8;
+        for (int e = 0; e < N; ++e) y[e] = s != 0.f ? rintf(x[e] / s) : 0.f;
+    }
+#pragma unroll
+    for (int w = 0; w < N / 4; ++w) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            v |= ((uint32_t)(int32_t)fminf(fmaxf(y[4 * w + b], -127.f), 127.f) & 0xffu) << (8 * b);
+        packed[w] = v;
+    }
 }
 
-__global__ __launch_bounds__(PT) void k_stats_kernel(const PassParams P) {
+// ---- the K passes of the int8-QK arm: MODE K_STATS writes ks, K_QUANT reads
+// ks and writes k8, K_BOTH writes both from one read of K (the results of the
+// two separate passes, bit for bit: the same arithmetic on the same values).
+// A workgroup takes KP_CPT * PT 16-byte chunks of consecutive (token, KV head)
+// rows of one request, KP_CPT per thread; a row's LPR lanes are consecutive
+// threads of one wave.  Each thread issues its chunks' block-table loads
+// together, then their row (and scale) loads together, before it reduces
+// anything, so a row costs one round trip rather than a chain of them; it
+// keeps the raw 16-byte words (four registers a chunk) and converts them to
+// fp32 where they are used, so that all its chunks stay in flight and the
+// grid of a long request is resident at once.
+enum KPassMode { K_STATS = 1, K_QUANT = 2, K_BOTH = 3 };
+constexpr int KP_CPT = 4;
+
+// value e of a chunk: a bf16 value, or an int8 code times the row's scale (fp32)
+template <bool SRC_I8>
+__device__ __forceinline__ float kval(const u32x4 &w, float s, int e) {
+    if constexpr (SRC_I8)
+        return (float)(int8_t)((w[e >> 2] >> ((e & 3) * 8)) & 0xff) * s;
+    else
+        return (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]);
+}
+
+template <int D, bool SRC_I8, int MODE>
+__global__ __launch_bounds__(PT) void k_pass_kernel(const PassParams P) {
+    constexpr int EPC = SRC_I8 ? 16 : 8;            // values per 16-byte chunk
+    constexpr int LPR = D / EPC;                    // lanes per row
+    constexpr int RPG = PT * KP_CPT / LPR;          // rows per workgroup step
+    static_assert(LPR <= 64 && 64 % LPR == 0, "a row's lanes share a wave");
     const int r = blockIdx.y;
     int L;
     if (!request_ok(P, r, L)) return;
-    const int lpr = P.D * (P.src_int8 ? 1 : 2) / 16;   // lanes per row (power of two <= 32)
-    const int sub = threadIdx.x % lpr, rl = threadIdx.x / lpr, rpw = PT / lpr;
     const int64_t nrows = (int64_t)L * P.Hkv;
     const int64_t row0 = (int64_t)P.cu_ctx[r] * P.Hkv;
-    for (int64_t row = (int64_t)blockIdx.x * rpw + rl; row < nrows; row += (int64_t)gridDim.x * rpw) {
-        const int t = (int)((uint32_t)row / (uint32_t)P.Hkv), g = (int)((uint32_t)row % (uint32_t)P.Hkv);
-        int64_t off = 0, soff = 0;
-        const bool ok = pass_row(P, r, t, g, off, soff);
-        float x[16];
-        const int n = chunk_values(P, off, soff, sub, ok, x);
-        float amax = 0.f;
-        for (int e = 0; e < n; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        for (int m = 1; m < lpr; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-        if (sub == 0) ((float *)P.dst)[row0 + row] = amax / 127.0f;
-    }
-}
-
-__device__ __forceinline__ uint32_t quant4(const float *x, float s) {
-    uint32_t packed = 0;
+    const int sub = threadIdx.x % LPR;
+    float *ks_out = (float *)P.dst;
+    int8_t *k8_out = (int8_t *)(MODE == K_BOTH ? P.dst2 : P.dst);
+    for (int64_t base = (int64_t)blockIdx.x * RPG; base < nrows; base += (int64_t)gridDim.x * RPG) {
+        auto row_of = [&](int c) -> int64_t { return base + (threadIdx.x + c * PT) / LPR; };
+        int64_t off[KP_CPT], soff[KP_CPT];
+        bool ok[KP_CPT];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        float y = s != 0.f ? rintf(x[b] / s) : 0.f;
-        y = fminf(fmaxf(y, -127.f), 127.f);
-        packed |= ((uint32_t)(int32_t)y & 0xffu) << (8 * b);
-    }
-    return packed;
-}
-
-__global__ __launch_bounds__(PT) void k_quant_kernel(const PassParams P) {
-    const int r = blockIdx.y;
-    int L;
-    if (!request_ok(P, r, L)) return;
-    const int lpr = P.D * (P.src_int8 ? 1 : 2) / 16;
-    const int sub = threadIdx.x % lpr, rl = threadIdx.x / lpr, rpw = PT / lpr;
-    const int64_t nrows = (int64_t)L * P.Hkv;
-    const int64_t row0 = (int64_t)P.cu_ctx[r] * P.Hkv;
-    for (int64_t row = (int64_t)blockIdx.x * rpw + rl; row < nrows; row += (int64_t)gridDim.x * rpw) {
-        const int t = (int)((uint32_t)row / (uint32_t)P.Hkv), g = (int)((uint32_t)row % (uint32_t)P.Hkv);
-        int64_t off = 0, soff = 0;
-        const bool ok = pass_row(P, r, t, g, off, soff);
-        float x[16];
-        const int n = chunk_values(P, off, soff, sub, ok, x);
-        const float s = P.ks[row0 + row];
-        int8_t *dst = (int8_t *)P.dst + (row0 + row) * P.D + sub * n;
-        if (n == 16) {
-            *(u32x4 *)dst = u32x4{quant4(x, s), quant4(x + 4, s), quant4(x + 8, s), quant4(x + 12, s)};
-        } else {
-            *(u32x2 *)dst = u32x2{quant4(x, s), quant4(x + 4, s)};
+        for (int c = 0; c < KP_CPT; ++c) {
+            const int64_t row = row_of(c);
+            const int t = (int)((uint64_t)row / (uint32_t)P.Hkv), g = (int)((uint64_t)row % (uint32_t)P.Hkv);
+            off[c] = soff[c] = 0;
+            ok[c] = row < nrows && pass_row(P, r, t, g, off[c], soff[c]);
+        }
+        u32x4 w[KP_CPT];
+        float sc[KP_CPT], ks_in[KP_CPT];
+#pragma unroll
+        for (int c = 0; c < KP_CPT; ++c) {
+            const char *src = (const char *)P.src + (off[c] + sub * EPC) * (SRC_I8 ? 1 : 2);
+            w[c] = ok[c] ? *(const u32x4 *)src : u32x4{0, 0, 0, 0};
+            sc[c] = SRC_I8 ? (ok[c] ? P.src_scales[soff[c]] : 0.f) : 1.f;
+            if constexpr (MODE == K_QUANT) ks_in[c] = row_of(c) < nrows ? P.ks[row0 + row_of(c)] : 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < KP_CPT; ++c) {
+            const int64_t row = row_of(c);
+            float s;
+            int cmax = 0;   // the largest |code| of this lane's chunk (int8 source)
+            if constexpr (SRC_I8) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int c8 = (int)(int8_t)((w[c][e >> 2] >> ((e & 3) * 8)) & 0xff);
+                    cmax = max(cmax, c8 < 0 ? -c8 : c8);
+                }
+            }
+            if constexpr ((MODE & K_STATS) != 0) {
+                float amax = 0.f;
+                if constexpr (SRC_I8) {
+                    // max |code * s| = max |code| * |s|: rounding is monotonic.  A
+                    // NaN product counts as absent, as fmaxf skips NaN values
+                    const float am = (float)cmax * fabsf(sc[c]);
+                    amax = am == am ? am : 0.f;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) amax = fmaxf(amax, fabsf(kval<SRC_I8>(w[c], sc[c], e)));
+                }
+#pragma unroll
+                for (int m = 1; m < LPR; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+                s = amax / 127.0f;
+            } else {
+                s = ks_in[c];
+            }
+            if (row >= nrows) continue;
+            if constexpr ((MODE & K_QUANT) != 0) {
+                uint32_t pk[EPC / 4];
+                // an int8 row whose new scale is its pool scale, bit for bit (finite,
+                // > 0), keeps its codes: x / s = RN(code * s) / s = code (1 + d) with
+                // |code d| <= 128 * 2^-24, which rounds to code.  Only a -128 code
+                // would then need its clamp, so those chunks take the general path
+                bool keep = false;
+                if constexpr (SRC_I8) keep = s == sc[c] && s > 0.f && s <= 3.4028234663852886e38f && cmax <= 127;
+                if (keep) {
+#pragma unroll
+                    for (int q = 0; q < EPC / 4; ++q) pk[q] = w[c][q];
+                } else {
+                    float x[EPC];
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) x[e] = kval<SRC_I8>(w[c], sc[c], e);
+                    quant_codes<EPC>(x, s, pk);
+                }
+                int8_t *dst = k8_out + (row0 + row) * D + sub * EPC;
+                if constexpr (EPC == 16)
+                    *(u32x4 *)dst = u32x4{pk[0], pk[1], pk[2], pk[3]};
+                else
+                    *(u32x2 *)dst = u32x2{pk[0], pk[1]};
+            }
+            if constexpr ((MODE & K_STATS) != 0)
+                if (sub == 0) ks_out[row0 + row] = s;
         }
     }
 }
@@ -230,8 +309,11 @@ __global__ __launch_bounds__(PT) void store_int8_kernel(const PassParams P) {
         }
         if (!ok) continue;
         const float ks = ka / 127.0f, vs = va / 127.0f;
-        *(u32x2 *)((int8_t *)P.dst + off + sub * 8) = u32x2{quant4(k, ks), quant4(k + 4, ks)};
-        *(u32x2 *)((int8_t *)P.dst2 + off + sub * 8) = u32x2{quant4(v, vs), quant4(v + 4, vs)};
+        uint32_t pk[2], pv[2];
+        quant_codes<8>(k, ks, pk);
+        quant_codes<8>(v, vs, pv);
+        *(u32x2 *)((int8_t *)P.dst + off + sub * 8) = u32x2{pk[0], pk[1]};
+        *(u32x2 *)((int8_t *)P.dst2 + off + sub * 8) = u32x2{pv[0], pv[1]};
         if (sub == 0) {
             P.dst_scales[soff] = ks;
             P.dst2_scales[soff] = vs;
@@ -293,14 +375,31 @@ static dim3 pass_grid(const PassParams &p, int row_bytes) {
     return dim3((uint32_t)x, (uint32_t)p.num_reqs);
 }
 
-hipError_t launch_k_stats(const PassParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(k_stats_kernel, pass_grid(p, p.D * (p.src_int8 ? 1 : 2)), dim3(PT), 0, s, p);
+template <int D, int MODE>
+static void launch_k_pass_d(const PassParams &p, dim3 grid, hipStream_t s) {
+    if (p.src_int8)
+        hipLaunchKernelGGL((k_pass_kernel<D, true, MODE>), grid, dim3(PT), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_pass_kernel<D, false, MODE>), grid, dim3(PT), 0, s, p);
+}
+template <int MODE>
+static hipError_t launch_k_pass(const PassParams &p, hipStream_t s) {
+    const int lpr = p.D * (p.src_int8 ? 1 : 2) / 16;
+    const int64_t rpg = (int64_t)PT * KP_CPT / lpr;
+    int64_t x = ((int64_t)p.max_ctx * p.Hkv + rpg - 1) / rpg;
+    x = x < 1 ? 1 : (x > 65536 ? 65536 : x);
+    const dim3 grid((uint32_t)x, (uint32_t)p.num_reqs);
+    switch (p.D) {
+        case 64: launch_k_pass_d<64, MODE>(p, grid, s); break;
+        case 128: launch_k_pass_d<128, MODE>(p, grid, s); break;
+        case 256: launch_k_pass_d<256, MODE>(p, grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
-hipError_t launch_k_quant(const PassParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(k_quant_kernel, pass_grid(p, p.D * (p.src_int8 ? 1 : 2)), dim3(PT), 0, s, p);
-    return hipGetLastError();
-}
+hipError_t launch_k_stats(const PassParams &p, hipStream_t s) { return launch_k_pass<K_STATS>(p, s); }
+hipError_t launch_k_quant(const PassParams &p, hipStream_t s) { return launch_k_pass<K_QUANT>(p, s); }
+hipError_t launch_k_stats_quant(const PassParams &p, hipStream_t s) { return launch_k_pass<K_BOTH>(p, s); }
 hipError_t launch_fp8_dequant(const PassParams &p, hipStream_t s) {
     PassParams g = p;
     if (p.cu_new) g.max_ctx = p.max_new;   // append: the grid covers the chunk's rows only

@@ -30,7 +30,7 @@ PA_STAGE_NONE, PA_STAGE_IMAGES, PA_STAGE_SCHEDULE, PA_STAGE_ATTENTION = 0, 1, 2,
 PA_STAGE_MERGE, PA_STAGE_PASS = 4, 5
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_bf16_noalloc", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
-                "pa_prefill_int8kv_splitkv", "pa_prefill_fp8kv", "pa_k_stats", "pa_k_quant",
+                "pa_prefill_int8kv_splitkv", "pa_prefill_fp8kv", "pa_k_stats", "pa_k_quant", "pa_k_stats_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_store_kv_int8", "pa_store_kv_fp8",
                 "pa_gather_kv", "pa_test_inject_failure",
                 "pa_peak_probe", "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
@@ -76,6 +76,7 @@ def lib():
             "pa_prefill_int8kv_splitkv": [pa, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
             "pa_k_stats": [pa, vp, i32, vp, vp, vp, vp],
             "pa_k_quant": [pa, vp, i32, vp, vp, vp, vp, vp],
+            "pa_k_stats_quant": [pa, vp, i32, vp, vp, vp, vp, vp],
             "pa_prefill_int8qk": [pa, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, sz, vp],
             "pa_fp8_dense_dequant": [pa, vp, vp, vp, vp, i32, vp, vp, vp],
             "pa_gather_kv": [pa, vp, i32, vp, vp, vp],
@@ -294,6 +295,13 @@ def pa_k_quant(p: Paged, k_pool, k_pool_scales, cu_ctx, ks, k8, stream=None):
     _check(lib().pa_k_quant(C.byref(a), _p(k_pool), _kdtype(k_pool), _p(k_pool_scales),
                             _p(cu_ctx), _p(ks), _p(k8), _stream(stream)), "pa_k_quant")
     return k8
+
+
+def pa_k_stats_quant(p: Paged, k_pool, k_pool_scales, cu_ctx, ks, k8, stream=None):
+    a = p.args()
+    _check(lib().pa_k_stats_quant(C.byref(a), _p(k_pool), _kdtype(k_pool), _p(k_pool_scales),
+                                  _p(cu_ctx), _p(ks), _p(k8), _stream(stream)), "pa_k_stats_quant")
+    return ks, k8
 
 
 def pa_prefill_int8qk(p: Paged, q, k8, ks, cu_ctx, v_pool, v_scales, out, ws=None,

@@ -140,6 +140,15 @@ class DevCase:
         ops.pa_k_quant(p, self.k_pool, self.k_scales, self.cu_ctx, ks, k8)
         return ks, k8
 
+    def run_k_stats_quant(self, which=0):
+        """The fused pass (pa_k_stats_quant) into NaN / 99-filled buffers."""
+        w = self.w
+        total = int(w.ctx_lens.sum())
+        ks = torch.full((total, w.num_kv_heads), float("nan"), dtype=torch.float32, device=DEV)
+        k8 = torch.full((total, w.num_kv_heads, w.head_dim), 99, dtype=torch.int8, device=DEV)
+        ops.pa_k_stats_quant(self.paged(which), self.k_pool, self.k_scales, self.cu_ctx, ks, k8)
+        return ks, k8
+
     def run_int8qk(self, which=0, out_dtype=torch.float32):
         ks, k8 = self.run_k_passes(which)
         o = self.out(out_dtype)

@@ -108,9 +108,9 @@ def test_bigpool_int8_both_arms(orc):
     ks_ref = orc.k_stats(tables[0], wq.ctx_lens, pools["k"], pools["k_scales"])
     k8_ref = orc.k_quant(tables[0], wq.ctx_lens, pools["k"], ks_ref, pools["k_scales"])
     for which in (0, 1):
-        ks, k8 = case.run_k_passes(which)
-        assert np.array_equal(ks.cpu().numpy().view(np.int32), ks_ref.view(np.int32))
-        assert np.array_equal(k8.cpu().numpy(), k8_ref)
+        for ks, k8 in (case.run_k_passes(which), case.run_k_stats_quant(which)):
+            assert np.array_equal(ks.cpu().numpy().view(np.int32), ks_ref.view(np.int32))
+            assert np.array_equal(k8.cpu().numpy(), k8_ref)
     rows = np.arange(int(wq.q_lens.sum()), dtype=np.int32)      # the whole chunk
     ref = G().oracle_rows(orc, wq, pools, rows, tables[0])
     # exact-QK arm (int8 KV dequantised in the tile)

@@ -55,6 +55,9 @@ def test_long_context_small_blocks(orc, fmt):
         assert np.array_equal(ks.cpu().numpy().view(np.int32), ks_ref.view(np.int32))
         k8_ref = orc.k_quant(w.block_table, w.ctx_lens, pools["k"], ks_ref, pools.get("k_scales"))
         assert np.array_equal(k8.cpu().numpy(), k8_ref)
+        ks2, k82 = case.run_k_stats_quant()       # the fused pass: the same bits
+        assert np.array_equal(ks2.cpu().numpy().view(np.int32), ks_ref.view(np.int32))
+        assert np.array_equal(k82.cpu().numpy(), k8_ref)
         emu = orc.prefill_int8qk(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, k8_ref, ks_ref,
                                  pools["v"], w.softmax_scale, v_scales=pools.get("v_scales"),
                                  rows=rows)

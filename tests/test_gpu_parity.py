@@ -133,6 +133,9 @@ def test_small_int8qk(orc, c, fmt):
     k8_ref = orc.k_quant(wq.block_table, wq.ctx_lens, pools["k"], ks_ref, pools.get("k_scales"))
     assert np.array_equal(bits(ks), ks_ref.view(np.int32))
     assert np.array_equal(k8.cpu().numpy(), k8_ref)
+    ks2, k82 = case.run_k_stats_quant()          # the fused pass: the same bits
+    assert np.array_equal(bits(ks2), ks_ref.view(np.int32))
+    assert np.array_equal(k82.cpu().numpy(), k8_ref)
     # short contexts: the arm's own quantisation error is larger than the long-
     # context gate, so the reference is the arm evaluated exactly by the oracle
     emu = orc.prefill_int8qk(wq.block_table, wq.cu_q_lens, wq.ctx_lens, wq.q, k8_ref, ks_ref,

@@ -97,6 +97,10 @@ def test_entry_point_specific_errors():
     assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_F32, None, p, p, None) == ops.PA_ERR_UNSUPPORTED
     assert L.pa_k_stats(C.byref(a), p, ops.PA_DTYPE_INT8, None, p, p, None) == ops.PA_ERR_NULL
     assert L.pa_k_quant(C.byref(a), p, ops.PA_DTYPE_BF16, None, p, p, None, None) == ops.PA_ERR_NULL
+    assert L.pa_k_stats_quant(C.byref(a), p, ops.PA_DTYPE_BF16, None, p, p, None, None) == ops.PA_ERR_NULL
+    assert L.pa_k_stats_quant(C.byref(a), p, ops.PA_DTYPE_INT8, None, p, p, p, None) == ops.PA_ERR_NULL
+    assert L.pa_k_stats_quant(C.byref(a), p, ops.PA_DTYPE_F32, None, p, p, p, None) == ops.PA_ERR_UNSUPPORTED
+    assert L.pa_k_stats_quant(C.byref(a), p, ops.PA_DTYPE_BF16, None, p, p, odd, None) == ops.PA_ERR_SHAPE
     assert L.pa_prefill_int8qk(C.byref(a), p, p, p, p, p, ops.PA_DTYPE_FP8_E4M3, None, p, 0,
                                p, big, None) == ops.PA_ERR_UNSUPPORTED
     assert L.pa_fp8_dense_dequant(C.byref(a), p, p, p, p, 8, p, p, None) == ops.PA_ERR_SHAPE
