@@ -87,9 +87,10 @@ constexpr float RESCALE_SLACK = 8.0f;   // lazy-rescale threshold, log2 units
 #define PA_PV_IN_A 0
 #endif
 // the int8-QK arm's phase A has half as many QK MFMAs for the same exponentials,
-// so it takes PV MFMAs into phase A as well (measured: 5 % faster than none)
+// so it takes PV MFMAs into phase A as well: 12 per 24 PV-capable slots (6 of
+// its 32 PV MFMAs) measured best, 3 % ahead of 48 (and of none)
 #ifndef PA_PV_IN_A_QK8
-#define PA_PV_IN_A_QK8 48
+#define PA_PV_IN_A_QK8 12
 #endif
 constexpr int QK_AHEAD = PA_QK_AHEAD;
 constexpr int PV_IN_A = PA_PV_IN_A;      // PV MFMAs in phase A per 24 of its PV-capable slots
@@ -158,6 +159,13 @@ static_assert(hstep_uniform(2) && hstep_uniform(4) && hstep_uniform(8) && hstep_
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void *base) {
     // raw buffer, stride 0, no range limit that any offset here can reach
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+// a raw buffer of `bytes` bytes from base: a lane whose offset (voffset plus
+// the instruction's; the soffset takes no part in this check) reaches past it
+// reads zeros, so a copy needs no branch for rows past the end of its data
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_range(const void *base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
 }
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char *lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
@@ -380,8 +388,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         } else if constexpr (C::K_I8) {
             return KSrc{rsrc_at(P.k_img + (img_base + (int64_t)kt * P.Hkv) * k_image_bytes(D)), 0u};
         } else if constexpr (C::QK8) {
-            // dense k8 rows of this request: [cu_ctx[r] + key][Hkv][D]
-            return KSrc{rsrc_at((const char *)P.k + (k8_row0 * P.Hkv + g) * D), 0u};
+            // dense k8 rows of this request: [cu_ctx[r] + key][Hkv][D], from the
+            // tile's first key on, the range ending with key n_keys - 1's row
+            const int64_t tile_off = (int64_t)kt * BN * k8_rowb;
+            return KSrc{rsrc_range((const char *)P.k + (k8_row0 * P.Hkv + g) * D + tile_off,
+                                   (int64_t)(n_keys - 1) * k8_rowb + D - tile_off), 0u};
         } else {
             return KSrc{rsrc_at(P.k), 0u};   // per-lane addresses below
         }
@@ -389,15 +400,17 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     auto k_copy = [&](const KSrc &src, int kt, int stage, int i) PA_INL {
         char *kl = kstage(stage);
         const int kbase = kt * BN;
-        if (i == C::K_PER_WAVE) {   // per-key scales
+        // no branch in a step's copies: a branch splits the step into blocks, and
+        // the compiler then sinks the next tile's post-processing below it, out
+        // of the PV MFMA slots it was placed between
+        if (i == C::K_PER_WAVE) {   // per-key scales, copied by every wave (same bytes)
             if constexpr (C::K_I8) {
-                if (wave_u == NWAVE - 2) bdma4(src.rs, k_key_lane * 4, BN * 2 * D, kl + C::K_BYTES);
+                bdma4(src.rs, k_key_lane * 4, BN * 2 * D, kl + C::K_BYTES);
             } else if constexpr (C::QK8) {
-                if (wave_u == NWAVE - 2) {
-                    const int key = kbase + k_key_lane;
-                    const auto ks = rsrc_at(P.kscale + k8_row0 * P.Hkv + g);
-                    bdma4(ks, (uint32_t)((key < n_keys ? key : 0) * P.Hkv * 4), 0, kl + C::K_BYTES);
-                }
+                // keys past the context read zeros (their logits are masked)
+                const auto ks = rsrc_range(P.kscale + (k8_row0 + kbase) * P.Hkv + g,
+                                           (int64_t)(n_keys - 1 - kbase) * P.Hkv * 4 + 4);
+                bdma4(ks, (uint32_t)(k_key_lane * P.Hkv * 4), 0, kl + C::K_BYTES);
             }
             return;
         }
@@ -420,14 +433,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         } else if constexpr (C::K_I8) {
             bdma16(src.rs, k_lane_src, q * 1024, dst);
         } else {
-            const int key0 = kbase + q * C::RPI;
-            if (kbase + BN <= n_keys) {
-                bdma16(src.rs, k_lane_src, (uint32_t)(key0 * k8_rowb), dst);
-            } else {
-                // last tile: rows past the context read the request's row 0
-                const bool ok = key0 + k_sub < n_keys;
-                bdma16(src.rs, ok ? (uint32_t)(key0 * k8_rowb) + k_lane_src : (uint32_t)(k_chunk * 16), 0, dst);
-            }
+            // rows past the context (last tile) fall outside the tile's range: zeros
+            bdma16(src.rs, k_lane_src + (uint32_t)(q * C::RPI * k8_rowb), 0, dst);
         }
     };
     constexpr int NKC = C::K_PER_WAVE + (C::K_SCALED ? 1 : 0);   // K copy instructions per wave
