@@ -239,6 +239,59 @@ int pa_prefill_int8kv_splitkv(const pa_paged_args *args, const void *q, const in
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_verify_bf16 / pa_verify_int8kv -- decode-shaped attention: a few query
+ * tokens per request against a long cached context, with per-range partial
+ * results and a combine step (HyperQwen PR #91, PR body: the spec-decode
+ * verify attention, 8 drafted tokens at a 60,000-token context).  The same
+ * attention as pa_prefill_bf16 / pa_prefill_int8kv (bottom-right causal or
+ * full, GQA, the same pools and strides), computed by a kernel shaped for
+ * few columns and many keys: each work item holds 32 (chunk row, q head of
+ * the KV head's group) columns and a range of keys, and its waves split the
+ * keys.  The pools are read as they are: no workspace, no tile images; int8
+ * codes are read as codes.
+ *
+ *   num_splits  1 .. PA_MAX_SPLITS.  With 16-key slabs n = ceil(L_r / 16),
+ *               split s takes slabs [floor(s n / S), floor((s + 1) n / S))
+ *               of every column tile (S = num_splits); a split with no slab
+ *               takes no key.
+ *   o_part      fp32 [num_reqs, max_q_len, Hq, num_splits, D]: for chunk row
+ *               i of request r (at r * max_q_len + i; rows i >= Lq_r are not
+ *               written), split s's attention over its range, normalised by
+ *               its own row sum; zeros for a row that sees none of the
+ *               range's keys.  NULL allowed with 1 split.
+ *   lse_part    fp32 [num_reqs, max_q_len, Hq, num_splits]: log(sum_j exp(scale
+ *               <q, K_j>)) over the range's keys the row sees, natural log;
+ *               -inf where it sees none.  NULL allowed with 1 split.
+ *   out         [sum Lq, Hq, D] of out_dtype: sum_s e^{lse_s - lse} O_s (one
+ *               split: the attention itself)
+ *   lse         fp32 [sum Lq, Hq] or NULL: the whole row's log-sum-exp
+ * Precision: QK^T products are exact (bf16 Q times bf16 K, or times the int8
+ * code, whose per-token-head scale then multiplies the logit) with fp32
+ * sums; the softmax runs in fp32; P (times the V scale, for int8) enters the
+ * PV product as a pair of bf16 values hi + lo (about 2^-17 relative) against
+ * V itself (bf16) or its exact int8 code, with fp32 accumulation.  P is taken
+ * as 2^-40 times its value, a factor that cancels, so no sum overflows for any
+ * finite bf16 V (int8: code times scale below 2^121) in contexts below 2^24
+ * keys.  Products below fp32's normal range (2^-126) may flush to zero.
+ * flags are ignored.  Errors as pa_prefill_bf16 / pa_prefill_int8kv (without
+ * the workspace checks), plus PA_ERR_SHAPE for num_splits out of range or a
+ * misaligned o_part (16 bytes), PA_ERR_NULL for a NULL o_part / lse_part
+ * with more than one split, PA_ERR_TOO_LARGE for more than 65,535 requests
+ * or 2^31 work items (requests x Hkv x 32-column tiles x num_splits, or
+ * requests x max_q_len x Hq x D / 64 merge waves).
+ * Block sizes that are a multiple of 16 take the fast path (one cache block
+ * per slab); others are served with per-row addresses, more slowly.
+ */
+int pa_verify_bf16(const pa_paged_args *args, const void *q, const void *k_pool,
+                   const void *v_pool, int32_t num_splits, float *o_part, float *lse_part,
+                   void *out, int32_t out_dtype, float *lse, hipStream_t stream);
+
+int pa_verify_int8kv(const pa_paged_args *args, const void *q, const int8_t *k_pool,
+                     const int8_t *v_pool, const float *k_scales, const float *v_scales,
+                     int32_t num_splits, float *o_part, float *lse_part, void *out,
+                     int32_t out_dtype, float *lse, hipStream_t stream);
+
+/*
  * pa_prefill_fp8kv -- attention straight over an fp8 e4m3fn pool with one
  * scale per tensor, the A/B arm of the one-time dense dequant (vllm.cpp PR
  * #3360, "What changed": its VT_ATTN_FP8_DENSE=0 switch keeps the per-read

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_kv_prefill.so")
 SOURCES = ["pa_attention.hip", "pa_images.hip", "pa_passes.hip", "pa_probe.hip", "pa_noalloc.hip",
-           "pa_api.cpp"]
+           "pa_verify.hip", "pa_api.cpp"]
 HEADERS = ["pa_device.h", "pa_kernels.h", "pa_layout.h"]
 PUBLIC_HEADER = os.path.join(ROOT, "include", "paged_kv_prefill.h")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

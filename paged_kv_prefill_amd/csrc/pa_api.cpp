@@ -300,6 +300,68 @@ int prefill_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool,
     return run_attention(a, KIND_I8KV, p, so, out, out_dtype, stream);
 }
 
+// decode-shaped attention (pa_verify_bf16 / pa_verify_int8kv)
+int verify(const pa_paged_args *a, bool int8, const void *q, const void *k_pool, const void *v_pool,
+           const float *k_scales, const float *v_scales, int32_t num_splits, float *o_part,
+           float *lse_part, void *out, int32_t out_dtype, float *lse, hipStream_t stream) {
+    int rc = check_common(a, int8 ? 1 : 2, true);
+    if (rc) return rc;
+    if ((rc = check_out(q, out, out_dtype))) return rc;
+    if (!k_pool || !v_pool) return PA_ERR_NULL;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_SHAPE;
+    if (int8 && ((rc = check_scales(a, k_scales)) || (rc = check_scales(a, v_scales)))) return rc;
+    if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return PA_ERR_SHAPE;
+    if (num_splits > 1) {
+        if (!o_part || !lse_part) return PA_ERR_NULL;
+        if (!aligned16(o_part)) return PA_ERR_SHAPE;
+    }
+    const int32_t group = a->num_q_heads / a->num_kv_heads;
+    const int64_t ctiles = verify_col_tiles(a->max_q_len, group);
+    const int64_t items = (int64_t)a->num_reqs * a->num_kv_heads * ctiles * num_splits;
+    if (items >= ((int64_t)1 << 31) || a->num_reqs > 65535) return PA_ERR_TOO_LARGE;
+    // merge waves: one per (request, chunk row, q head, 64 output elements)
+    if ((int64_t)a->num_reqs * a->max_q_len * a->num_q_heads * (a->head_dim / 64) >= ((int64_t)1 << 31))
+        return PA_ERR_TOO_LARGE;
+    VerifyParams p{};
+    p.bt = a->block_table;
+    p.stride_bt = a->stride_bt;
+    p.cu_q = a->cu_q_lens;
+    p.ctx_lens = a->ctx_lens;
+    p.num_reqs = a->num_reqs;
+    p.Hq = a->num_q_heads;
+    p.Hkv = a->num_kv_heads;
+    p.group = group;
+    p.block_size = a->block_size;
+    p.max_ctx = a->max_ctx_len;
+    p.bsdiv = make_fastdiv((uint32_t)a->block_size);
+    p.num_blocks = a->num_blocks;
+    p.stride_block = a->stride_block;
+    p.stride_tok = a->stride_tok;
+    p.stride_head = a->stride_head;
+    p.stride_sblock = a->stride_sblock;
+    p.stride_stok = a->stride_stok;
+    p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+    p.causal = a->causal;
+    p.ctiles = (int32_t)ctiles;
+    p.splits = num_splits;
+    p.q = q;
+    p.k = k_pool;
+    p.v = v_pool;
+    p.kscale = int8 ? k_scales : nullptr;
+    p.vscale = int8 ? v_scales : nullptr;
+    p.max_q = a->max_q_len;
+    p.out = out;
+    p.out_bf16 = out_dtype == PA_DTYPE_BF16;
+    p.lse = lse;
+    if (num_splits > 1) {
+        p.o_part = o_part;
+        p.lse_part = lse_part;
+    }
+    if ((rc = launch_stage(PA_STAGE_ATTENTION, [&] { return launch_verify(int8, a->head_dim, p, stream); }))) return rc;
+    if (num_splits == 1) return PA_OK;
+    return launch_stage(PA_STAGE_MERGE, [&] { return launch_verify_merge(p, a->head_dim, stream); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -334,6 +396,20 @@ int pa_prefill_int8kv_splitkv(const pa_paged_args *a, const void *q, const int8_
     const SplitOut so{num_splits, o_part, lse_part, lse};
     return prefill_int8kv(a, q, k_pool, v_pool, k_scales, v_scales, &so, out, out_dtype, workspace,
                           workspace_bytes, stream);
+}
+
+int pa_verify_bf16(const pa_paged_args *a, const void *q, const void *k_pool, const void *v_pool,
+                   int32_t num_splits, float *o_part, float *lse_part, void *out, int32_t out_dtype,
+                   float *lse, hipStream_t stream) {
+    return verify(a, false, q, k_pool, v_pool, nullptr, nullptr, num_splits, o_part, lse_part, out, out_dtype,
+                  lse, stream);
+}
+
+int pa_verify_int8kv(const pa_paged_args *a, const void *q, const int8_t *k_pool, const int8_t *v_pool,
+                     const float *k_scales, const float *v_scales, int32_t num_splits, float *o_part,
+                     float *lse_part, void *out, int32_t out_dtype, float *lse, hipStream_t stream) {
+    return verify(a, true, q, k_pool, v_pool, k_scales, v_scales, num_splits, o_part, lse_part, out, out_dtype,
+                  lse, stream);
 }
 
 int pa_prefill_fp8kv(const pa_paged_args *a, const void *q, const uint8_t *k_pool,

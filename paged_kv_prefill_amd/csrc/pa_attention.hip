@@ -1083,24 +1083,21 @@ hipError_t launch_schedule(const AttnParams &p, int32_t max_q_len, hipStream_t s
 }
 
 // ---- split-KV merge (deterministic: the splits are summed in order).  One
-// wave per (chunk row, q head), D / 64 output elements per lane:
+// wave per (chunk row, q head, 64 consecutive output elements), one element
+// per lane:
 //     m = max_s lse_s,  w_s = e^{lse_s - m} (0 for an empty split),
 //     O = sum_s w_s O_s / sum_s w_s,  lse = m + ln sum_s w_s.
 constexpr int MERGE_THREADS = 256;
-#ifndef PA_MERGE_BATCH
-#define PA_MERGE_BATCH 32
-#endif
-constexpr int MERGE_BATCH = PA_MERGE_BATCH;   // splits whose partials are loaded together
+constexpr int MERGE_BATCH = 64;   // splits whose partials are loaded together (one per lane of a wave)
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(const MergeParams P) {
-    constexpr int PER = D / 64;
-    // one lane's PER consecutive fp32 of a partial row, as one load
-    using Vec = std::conditional_t<PER == 4, f32x4, std::conditional_t<PER == 2, f32x2, float>>;
-    static_assert(sizeof(Vec) == PER * sizeof(float), "merge vector");
+    constexpr int SEGS = D / 64;   // waves per (row, head)
     const int r = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t pair = (int64_t)blockIdx.x * (MERGE_THREADS / 64) + wave;   // row * Hq + head
+    const int64_t gw = (int64_t)blockIdx.x * (MERGE_THREADS / 64) + wave;
+    const int64_t pair = gw / SEGS;   // row * Hq + head
+    const int e0 = (int)(gw % SEGS) * 64 + lane;
     const int q0 = P.cu_q[r];
     const int Lq = P.cu_q[r + 1] - q0;
     const int L = P.ctx_lens[r];
@@ -1110,47 +1107,42 @@ __global__ __launch_bounds__(MERGE_THREADS) void merge_kernel(const MergeParams 
     if (pair >= (int64_t)Lq * P.Hq) return;
     const int64_t ph = (int64_t)q0 * P.Hq + pair;
     const float *ls = P.lse_part + ph * P.splits;
+    const float *op = P.o_part + ph * P.splits * D + e0;
+    // the first MERGE_BATCH splits' partials, issued before the maximum's
+    // loads so that one round trip brings both
+    float o[MERGE_BATCH];
+#pragma unroll
+    for (int j = 0; j < MERGE_BATCH; ++j) o[j] = j < P.splits ? op[(int64_t)j * D] : 0.f;
     // the maximum: each lane takes every 64th split, then the wave's maximum
     float m = -INFINITY;
     for (int s = lane; s < P.splits; s += 64) m = fmaxf(m, ls[s]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float acc = 0.f;
     float wsum = 0.f;
-    // the sums run over the splits in index order; MERGE_BATCH splits' loads are
-    // issued together before they are added
+    // the sums run over the splits in index order; split s0 + j's weight is
+    // computed by lane j and read by every lane
     for (int s0 = 0; s0 < P.splits; s0 += MERGE_BATCH) {
-        float l[MERGE_BATCH];
-        float o[MERGE_BATCH][PER];
+        if (s0 > 0) {
 #pragma unroll
-        for (int j = 0; j < MERGE_BATCH; ++j) {
-            const int s = s0 + j;
-            l[j] = s < P.splits ? ls[s] : -INFINITY;
-            const Vec v = *(const Vec *)(P.o_part + (ph * P.splits + (s < P.splits ? s : 0)) * D + lane * PER);
-            __builtin_memcpy(o[j], &v, sizeof(Vec));
+            for (int j = 0; j < MERGE_BATCH; ++j) o[j] = s0 + j < P.splits ? op[(int64_t)(s0 + j) * D] : 0.f;
         }
+        const float lj = s0 + lane < P.splits ? ls[s0 + lane] : -INFINITY;
+        const float wj = lj == -INFINITY ? 0.f : expf(lj - m);
 #pragma unroll
         for (int j = 0; j < MERGE_BATCH; ++j) {
-            if (l[j] == -INFINITY) continue;   // an empty split (its partial is not written)
-            const float w = expf(l[j] - m);
+            const float lv = __builtin_amdgcn_readlane(__float_as_int(lj), j) == __float_as_int(-INFINITY)
+                                 ? -INFINITY : 0.f;
+            if (lv == -INFINITY) continue;   // an empty split, or past the last (its partial may be unwritten)
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
             wsum += w;
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] += w * o[j][e];
+            acc += w * o[j];
         }
     }
     const float inv = 1.0f / wsum;
-    if constexpr (OUT_BF16) {
-        __bf16 *dst = (__bf16 *)P.out + ph * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) dst[e] = (__bf16)(acc[e] * inv);
-    } else {
-        float *dst = (float *)P.out + ph * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) dst[e] = acc[e] * inv;
-    }
-    if (P.lse && lane == 0) P.lse[ph] = m + logf(wsum);
+    if constexpr (OUT_BF16) ((__bf16 *)P.out)[ph * D + e0] = (__bf16)(acc * inv);
+    else ((float *)P.out)[ph * D + e0] = acc * inv;
+    if (P.lse && e0 == 0) P.lse[ph] = m + logf(wsum);
 }
 
 template <int D>
@@ -1162,8 +1154,8 @@ static void launch_merge_d(const MergeParams &p, bool out_bf16, dim3 grid, hipSt
 }
 
 hipError_t launch_merge(const MergeParams &p, bool out_bf16, int32_t max_q_len, hipStream_t stream) {
-    const int64_t pairs = (int64_t)max_q_len * p.Hq;
-    const int64_t gx = (pairs + MERGE_THREADS / 64 - 1) / (MERGE_THREADS / 64);
+    const int64_t waves = (int64_t)max_q_len * p.Hq * (p.D / 64);   // one per 64 output elements
+    const int64_t gx = (waves + MERGE_THREADS / 64 - 1) / (MERGE_THREADS / 64);
     if (gx <= 0) return hipSuccess;
     if (gx > 0x7fffffff || p.num_reqs > 65535 || p.splits < 1) return hipErrorInvalidValue;
     const dim3 grid((uint32_t)gx, (uint32_t)p.num_reqs);

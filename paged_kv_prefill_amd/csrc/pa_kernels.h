@@ -58,6 +58,36 @@ struct MergeParams {
     float *lse;                 // [sum Lq, Hq] fp32 or null
 };
 
+// Decode-shaped attention (pa_verify.hip): a few query rows per request
+// against a long context; waves split the keys.  Every pointer is device memory.
+struct VerifyParams {
+    const int32_t *bt;
+    int64_t stride_bt;
+    const int32_t *cu_q;
+    const int32_t *ctx_lens;
+    int32_t num_reqs, Hq, Hkv, group;
+    int32_t block_size, max_ctx;
+    FastDivHost bsdiv;
+    int64_t num_blocks;
+    int64_t stride_block, stride_tok, stride_head;
+    int64_t stride_sblock, stride_stok;
+    float scale_log2;           // softmax scale * log2(e)
+    int32_t causal;
+    int32_t ctiles;             // 32-column tiles per (request, kv head)
+    int32_t splits;             // key splits per column tile, >= 1
+    const void *q;              // bf16 [sum Lq, Hq, D]
+    const void *k;              // bf16 or int8 pool
+    const void *v;
+    const float *kscale;        // int8 pools: per-token-head scales
+    const float *vscale;
+    int32_t max_q;              // rows per request in o_part / lse_part (max_q_len)
+    float *o_part;              // [num_reqs, max_q, Hq, splits, D] fp32, or null: write out / lse directly
+    float *lse_part;            // [num_reqs, max_q, Hq, splits] fp32 (natural log)
+    void *out;                  // [sum Lq, Hq, D] (o_part null)
+    int32_t out_bf16;
+    float *lse;                 // [sum Lq, Hq] or null (o_part null)
+};
+
 enum AttnKind { KIND_BF16 = 0, KIND_I8KV = 1, KIND_QK8_VBF16 = 2, KIND_QK8_VI8 = 3 };
 
 // Per-token passes (K stats, K quant, fp8 dense dequant, gather).
@@ -125,6 +155,9 @@ hipError_t launch_attention(int kind, int head_dim, bool out_bf16, const AttnPar
                             int32_t max_q_len, hipStream_t stream);
 // O = sum_s exp(lse_s - lse) O_s, lse = log sum_s exp(lse_s), splits in order
 hipError_t launch_merge(const MergeParams &p, bool out_bf16, int32_t max_q_len, hipStream_t stream);
+hipError_t launch_verify(bool int8, int head_dim, const VerifyParams &p, hipStream_t stream);
+hipError_t launch_verify_merge(const VerifyParams &p, int head_dim, hipStream_t stream);
+int64_t verify_col_tiles(int32_t max_q_len, int32_t group);
 // key rows per 1 KB K copy of an attention kind (fixes the tile's key order)
 int attn_rows_per_copy(int kind, int head_dim);
 hipError_t launch_images(const ImageParams &p, int fmt, bool k_image, hipStream_t stream);

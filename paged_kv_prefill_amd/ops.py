@@ -30,7 +30,7 @@ PA_STAGE_NONE, PA_STAGE_IMAGES, PA_STAGE_SCHEDULE, PA_STAGE_ATTENTION = 0, 1, 2,
 PA_STAGE_MERGE, PA_STAGE_PASS = 4, 5
 
 ENTRY_POINTS = ["pa_prefill_bf16", "pa_prefill_bf16_noalloc", "pa_prefill_int8kv", "pa_prefill_bf16_splitkv",
-                "pa_prefill_int8kv_splitkv", "pa_prefill_fp8kv", "pa_k_stats", "pa_k_quant", "pa_k_stats_quant",
+                "pa_prefill_int8kv_splitkv", "pa_verify_bf16", "pa_verify_int8kv", "pa_prefill_fp8kv", "pa_k_stats", "pa_k_quant", "pa_k_stats_quant",
                 "pa_prefill_int8qk", "pa_fp8_dense_dequant", "pa_store_kv_int8", "pa_store_kv_fp8",
                 "pa_gather_kv", "pa_test_inject_failure",
                 "pa_peak_probe", "pa_workspace_bytes", "pa_status_string", "pa_build_id"]
@@ -73,6 +73,8 @@ def lib():
             "pa_prefill_int8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
             "pa_prefill_bf16_splitkv": [pa, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
             "pa_prefill_fp8kv": [pa, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp],
+            "pa_verify_bf16": [pa, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp],
+            "pa_verify_int8kv": [pa, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp],
             "pa_prefill_int8kv_splitkv": [pa, vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, sz, vp],
             "pa_k_stats": [pa, vp, i32, vp, vp, vp, vp],
             "pa_k_quant": [pa, vp, i32, vp, vp, vp, vp, vp],
@@ -266,6 +268,43 @@ def pa_prefill_int8kv_splitkv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, o
                                            _p(v_scales), int(num_splits), _p(o_part), _p(lse_part),
                                            _p(out), dt, _p(lse), wp, wn, _stream(stream)),
            "pa_prefill_int8kv_splitkv")
+    return out
+
+
+def verify_buffers(p: Paged, num_splits: int, device):
+    """fp32 partial buffers of the decode-shaped entry points: O
+    [num_reqs, max_q_len, Hq, S, D] and log-sum-exp [num_reqs, max_q_len, Hq, S]
+    (torch-owned; chunk row i of request r at r * max_q_len + i)."""
+    rows = p.ctx_lens.numel() * p.max_q_len
+    o = torch.empty((rows, p.num_q_heads, num_splits, p.head_dim), dtype=torch.float32, device=device)
+    lse = torch.empty((rows, p.num_q_heads, num_splits), dtype=torch.float32, device=device)
+    return o, lse
+
+
+def pa_verify_bf16(p: Paged, q, k_pool, v_pool, out, num_splits, o_part=None, lse_part=None,
+                   lse=None, stream=None):
+    """Decode-shaped attention (few query rows, long context) over a bf16 pool;
+    one split writes out directly, more go through o_part / lse_part (made
+    here when not given, see verify_buffers) and the merge."""
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    if num_splits > 1 and (o_part is None or lse_part is None):
+        o_part, lse_part = verify_buffers(p, num_splits, q.device)
+    _check(lib().pa_verify_bf16(C.byref(a), _p(q), _p(k_pool), _p(v_pool), int(num_splits), _p(o_part),
+                                _p(lse_part), _p(out), dt, _p(lse), _stream(stream)), "pa_verify_bf16")
+    return out
+
+
+def pa_verify_int8kv(p: Paged, q, k_pool, v_pool, k_scales, v_scales, out, num_splits, o_part=None,
+                     lse_part=None, lse=None, stream=None):
+    """pa_verify_bf16 over an int8 pool with per-token-head scales."""
+    a = p.args()
+    dt = PA_DTYPE_BF16 if out.dtype == torch.bfloat16 else PA_DTYPE_F32
+    if num_splits > 1 and (o_part is None or lse_part is None):
+        o_part, lse_part = verify_buffers(p, num_splits, q.device)
+    _check(lib().pa_verify_int8kv(C.byref(a), _p(q), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales),
+                                  int(num_splits), _p(o_part), _p(lse_part), _p(out), dt, _p(lse),
+                                  _stream(stream)), "pa_verify_int8kv")
     return out
 
 

@@ -130,6 +130,30 @@ class DevCase:
                                           self.v_scales, o, num_splits, o_part, lse_part, lse)
         return o, lse, o_part, lse_part
 
+    def run_verify(self, num_splits, arm="bf16", which=0, out_dtype=torch.float32, with_lse=True):
+        """Decode-shaped entry point (pa_verify_bf16 / pa_verify_int8kv);
+        returns (out, lse, o_part, lse_part), the buffers NaN-filled
+        beforehand so unwritten entries show (no partials with one split)."""
+        w = self.w
+        rows = int(w.q_lens.sum())
+        prow = w.num_reqs * int(w.q_lens.max())   # partial rows: (request, chunk row)
+        o_part = lse_part = None
+        if num_splits > 1:
+            o_part = torch.full((prow, w.num_q_heads, num_splits, w.head_dim), float("nan"),
+                                dtype=torch.float32, device=DEV)
+            lse_part = torch.full((prow, w.num_q_heads, num_splits), float("nan"),
+                                  dtype=torch.float32, device=DEV)
+        lse = torch.full((rows, w.num_q_heads), float("nan"), dtype=torch.float32, device=DEV) \
+            if with_lse else None
+        o = self.out(out_dtype)
+        p = self.paged(which)
+        if arm == "bf16":
+            ops.pa_verify_bf16(p, self.q, self.k_pool, self.v_pool, o, num_splits, o_part, lse_part, lse)
+        else:
+            ops.pa_verify_int8kv(p, self.q, self.k_pool, self.v_pool, self.k_scales, self.v_scales, o,
+                                 num_splits, o_part, lse_part, lse)
+        return o, lse, o_part, lse_part
+
     def run_k_passes(self, which=0):
         w = self.w
         total = int(w.ctx_lens.sum())

@@ -183,6 +183,35 @@ def test_split_kv_argument_errors():
     assert i8(C.byref(a), p, p, p, p, p, 4, p, None, p, 0, None, p, big, None) == ops.PA_ERR_NULL
 
 
+def test_verify_argument_errors():
+    """pa_verify_bf16 / pa_verify_int8kv: every call below fails validation
+    (split count, partial buffers, scales, sizes) before anything is enqueued;
+    one split needs no partial buffers."""
+    L = ops.lib()
+    a = _args()
+    p = C.c_void_p(4096)
+    odd = C.c_void_p(4100)
+    bf = L.pa_verify_bf16
+    i8 = L.pa_verify_int8kv
+    assert bf(None, p, p, p, 4, p, p, p, 0, None, None) == ops.PA_ERR_NULL
+    assert bf(C.byref(a), p, p, p, 0, p, p, p, 0, None, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(a), p, p, p, ops.PA_MAX_SPLITS + 1, p, p, p, 0, None, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(a), p, p, p, 4, None, p, p, 0, None, None) == ops.PA_ERR_NULL
+    assert bf(C.byref(a), p, p, p, 4, p, None, p, 0, None, None) == ops.PA_ERR_NULL
+    assert bf(C.byref(a), p, p, p, 4, odd, p, p, 0, None, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(a), p, p, p, 4, p, p, p, 5, None, None) == ops.PA_ERR_UNSUPPORTED
+    assert bf(C.byref(a), None, p, p, 4, p, p, p, 0, None, None) == ops.PA_ERR_NULL
+    assert bf(C.byref(a), p, None, p, 1, None, None, p, 0, None, None) == ops.PA_ERR_NULL
+    assert bf(C.byref(a), p, odd, p, 1, None, None, p, 0, None, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(_args(num_q_heads=3)), p, p, p, 1, None, None, p, 0, None, None) == ops.PA_ERR_SHAPE
+    assert bf(C.byref(_args(num_reqs=70000)), p, p, p, 4, p, p, p, 0, None, None) == ops.PA_ERR_TOO_LARGE
+    assert i8(C.byref(a), p, p, p, None, p, 1, None, None, p, 0, None, None) == ops.PA_ERR_NULL
+    assert i8(C.byref(a), p, p, p, p, None, 1, None, None, p, 0, None, None) == ops.PA_ERR_NULL
+    assert i8(C.byref(_args(stride_sblock=0)), p, p, p, p, p, 1, None, None, p, 0, None, None) == ops.PA_ERR_SHAPE
+    assert i8(C.byref(a), p, p, p, p, p, 4, None, p, p, 0, None, None) == ops.PA_ERR_NULL
+    assert i8(C.byref(_args(stride_tok=136)), p, p, p, p, p, 1, None, None, p, 0, None, None) == ops.PA_ERR_SHAPE
+
+
 def test_fp8kv_and_append_argument_errors():
     L = ops.lib()
     a = _args()
