@@ -24,8 +24,10 @@ counter profile when that was taken on this build, the CPU oracle's rate over
 the same 2,048-row chunk, and the other arms (the headline with a bf16 output, int8 KV
 exact-QK, int8-QK with its fused K pass (and the two separate passes), fp8 KV through the dense
 bf16 scratch, the batched 8-request chunk,
-split-KV on a short chunk and on a spec-decode verify at 60,000 context, the
-quantise-on-store writers) measured per call.
+split-KV on a short chunk and on a spec-decode verify at 60,000 context (the
+split prefill entries, and the decode-shaped verify entries warm and with the
+context rotating over four pool placements), the quantise-on-store writers)
+measured per call.
 """
 from __future__ import annotations
 
@@ -48,6 +50,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 DEV = "cuda"
+VERIFY_SPLITS = 64             # key splits of the decode-shaped verify call (one workgroup per CU)
 
 
 # ------------------------------------------------------------------ setup helpers
@@ -116,6 +119,24 @@ class Pools:
             synth.fill_pool(wp, self.v, dev(w.v))
             self.k_scale = torch.tensor([float(w.k_scale)], dtype=torch.float32, device=DEV)
             self.v_scale = torch.tensor([float(w.v_scale)], dtype=torch.float32, device=DEV)
+
+    def add_placement(self, block_table):
+        """Write the same context again at the blocks of another block table
+        (bf16 values, or int8 through the quantise-on-store writer)."""
+        w = self.w
+        wp = w.with_block_table(block_table)
+        if w.kv_format == "bf16":
+            synth.fill_pool(wp, self.k, dev_bf16(w.k))
+            synth.fill_pool(wp, self.v, dev_bf16(w.v))
+        elif w.kv_format == "int8" and w.int8_sources:
+            mc = int(w.ctx_lens.max())
+            whole = ops.Paged(dev(block_table), self.cu_ctx, self.ctx, mc, mc, w.block_size, w.num_blocks,
+                              w.num_q_heads, w.num_kv_heads, w.head_dim, w.softmax_scale)
+            ops.pa_store_kv_int8(whole, dev_bf16(w.k), dev_bf16(w.v), self.k, self.v, self.k_scales,
+                                 self.v_scales)
+        else:
+            raise ValueError("add_placement: bf16 or int8-source workloads only")
+        torch.cuda.synchronize()
 
     def paged(self, cu_q=None, ctx=None, max_q=None, max_ctx=None):
         w = self.w
@@ -456,7 +477,8 @@ def arm_splitkv(steps, warmup):
     60,000-token context (int8 per-token-head and bf16 KV) with 32 splits,
     whole calls (V image pass + attention + merge), attention + merge alone
     (images reused), and decode-loop steps (PA_FLAG_APPEND: only the last
-    tile's images rebuilt)."""
+    tile's images rebuilt); and the decode-shaped entry points on the same
+    verify (whole calls: kernel + merge)."""
     res = {}
     w = synth.config_bigpool_bf16()
     lq = 256
@@ -511,13 +533,43 @@ def arm_splitkv(steps, warmup):
         L, hkv, d = int(w.ctx_lens[0]), w.num_kv_heads, w.head_dim
         # algorithmic bytes: every K and V element (and int8 scale) of the context read once
         kv_bytes = 2 * L * hkv * d * (1 if fmt == "int8" else 2) + (2 * L * hkv * 4 if fmt == "int8" else 0)
+        # the decode-shaped entry point (no images: each call is the whole
+        # call), with the context at one placement (warm: it fits the 256 MB
+        # last-level cache between calls) and rotating over four placements
+        # (1 GB / 500 MB of distinct pool rows: every call reads HBM)
+        DS = VERIFY_SPLITS
+        nb = w.block_table.shape[1]
+        tables = [w.block_table] + [np.arange(k * 600, k * 600 + nb, dtype=np.int32)[None, :]
+                                    for k in range(3)]
+        for t in tables[1:]:
+            P.add_placement(t)
+        pas = []
+        for t in tables:
+            pp = P.paged()
+            pp.block_table = dev(t)
+            pas.append(pp)
+        vo, vl = ops.verify_buffers(p, DS, DEV)
+        if fmt == "bf16":
+            g = lambda pp: ops.pa_verify_bf16(pp, P.q, P.k, P.v, out, DS, vo, vl)
+        else:
+            g = lambda pp: ops.pa_verify_int8kv(pp, P.q, P.k, P.v, P.k_scales, P.v_scales, out, DS, vo, vl)
+        (t_dec,), _ = time_launches([lambda: g(pas[0])], steps, warmup)
+        t_rot, _ = time_launches([lambda pp=pp: g(pp) for pp in pas], steps, warmup)
+        t_rot = float(np.mean(t_rot))
         res[f"verify_60k_{fmt}"] = {
             "splits": S, "ms_call": t_call, "ms_images_ready": t_ready, "ms_append": t_app,
             "gbs_append": kv_bytes / t_app * 1e-6,
             "kv_bytes": kv_bytes, "gbs_call": kv_bytes / t_call * 1e-6,
             "gbs_images_ready": kv_bytes / t_ready * 1e-6,
-            "hbm_frac_images_ready": kv_bytes / t_ready * 1e-6 / PEAK_HBM_GBS}
-        del P, ws, o_part, lse_part
+            "hbm_frac_images_ready": kv_bytes / t_ready * 1e-6 / PEAK_HBM_GBS,
+            "decode_kernel": {
+                "entry": "pa_verify_" + ("bf16" if fmt == "bf16" else "int8kv"), "splits": DS,
+                "ms_call": t_dec, "gbs": kv_bytes / t_dec * 1e-6,
+                "hbm_frac": kv_bytes / t_dec * 1e-6 / PEAK_HBM_GBS,
+                "ms_call_rotating": t_rot, "gbs_rotating": kv_bytes / t_rot * 1e-6,
+                "hbm_frac_rotating": kv_bytes / t_rot * 1e-6 / PEAK_HBM_GBS,
+                "note": "whole calls (verify kernel + merge); rotating: four placements of the context"}}
+        del P, ws, o_part, lse_part, vo, vl
         torch.cuda.empty_cache()
     return res
 

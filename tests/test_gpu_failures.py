@@ -103,3 +103,32 @@ def test_pass_failure(orc):
     pools = synth.host_pools(G.host_workload(w, orc))
     ks_ref = orc.k_stats(w.block_table, w.ctx_lens, pools["k"], pools.get("k_scales"))
     assert np.array_equal(ks2.cpu().numpy().view(np.int32), ks_ref.view(np.int32))
+
+
+@pytest.mark.parametrize("stage", ["attention", "merge"])
+@pytest.mark.parametrize("fmt", ["bf16", "int8"])
+def test_verify_stage_failure(orc, stage, fmt):
+    """The decode-shaped entry points: a failing attention stage leaves the
+    partials and the output untouched; a failing merge leaves the output
+    untouched after the partials were written; the next call matches the
+    oracle."""
+    from paged_kv_prefill_amd import ops
+    G, w, case = _case(fmt)
+    p = case.paged()
+    o_part, lse_part = ops.verify_buffers(p, 4, "cuda")
+    o_part.fill_(float("nan"))
+    lse_part.fill_(float("nan"))
+    out = case.out()
+    arm = (lambda o: ops.pa_verify_bf16(p, case.q, case.k_pool, case.v_pool, o, 4, o_part, lse_part)) \
+        if fmt == "bf16" else \
+        (lambda o: ops.pa_verify_int8kv(p, case.q, case.k_pool, case.v_pool, case.k_scales, case.v_scales,
+                                        o, 4, o_part, lse_part))
+    ops.pa_test_inject_failure(ops.PA_STAGE_ATTENTION if stage == "attention" else ops.PA_STAGE_MERGE)
+    _fails(lambda: arm(out))
+    assert torch.isnan(out).all(), "no stage after the failing one ran"
+    assert torch.isnan(lse_part).all() == (stage == "attention")
+    arm(out)
+    torch.cuda.synchronize()
+    wq = G.host_workload(w, orc)
+    ref = G.oracle_rows(orc, wq, synth.host_pools(wq), None)
+    assert float(np.max(np.abs(out.cpu().numpy() - ref))) <= ATOL

@@ -447,7 +447,7 @@ def test_bf16_output_is_the_rounded_fp32_output(arm):
 
 
 @pytest.mark.parametrize("bad", ["chunk_longer_than_context", "context_above_max", "context_beyond_table_row"])
-@pytest.mark.parametrize("arm", ["bf16", "split_bf16", "int8qk"])
+@pytest.mark.parametrize("arm", ["bf16", "split_bf16", "int8qk", "verify_bf16", "verify_int8kv"])
 def test_inconsistent_request_is_skipped(orc, bad, arm):
     """A request whose device lengths are inconsistent (chunk longer than its
     context, context above max_ctx_len, context beyond what its block-table row
@@ -456,7 +456,7 @@ def test_inconsistent_request_is_skipped(orc, bad, arm):
     from paged_kv_prefill_amd import ops
     g = gc()
     w = synth.make_case(160, [30, 20, 25], [100, 50, 80], 16, 8, 2, 64,
-                        kv_format="int8" if arm == "int8qk" else "bf16")
+                        kv_format="int8" if arm in ("int8qk", "verify_int8kv") else "bf16")
     case = g.DevCase(w)
     assert w.block_table.shape[1] == 7
     ctx = w.ctx_lens.copy()
@@ -478,6 +478,10 @@ def test_inconsistent_request_is_skipped(orc, bad, arm):
     elif arm == "split_bf16":
         o_part, lse_part = ops.split_buffers(int(w.q_lens.sum()), w.num_q_heads, w.head_dim, 3, "cuda")
         ops.pa_prefill_bf16_splitkv(p, case.q, case.k_pool, case.v_pool, out, 3, o_part, lse_part)
+    elif arm == "verify_bf16":
+        ops.pa_verify_bf16(p, case.q, case.k_pool, case.v_pool, out, 3)
+    elif arm == "verify_int8kv":
+        ops.pa_verify_int8kv(p, case.q, case.k_pool, case.v_pool, case.k_scales, case.v_scales, out, 3)
     else:
         total = int(w.ctx_lens.sum())
         ks = torch.full((total, w.num_kv_heads), float("nan"), dtype=torch.float32, device="cuda")
@@ -503,5 +507,5 @@ def test_inconsistent_request_is_skipped(orc, bad, arm):
                                  pools["v"], w.softmax_scale, v_scales=pools["v_scales"], rows=kept)
         vb = g.v_rounding_bound(orc, wq, pools, rows=kept)
     else:
-        ref = g.oracle_rows(orc, w, pools, kept)
+        ref = g.oracle_rows(orc, wq, pools, kept)
     assert np.all(np.abs(got[kept].astype(np.float64) - ref) <= ATOL + vb)
