@@ -306,8 +306,10 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
 
     // ---- this wave's slabs: lo + wave + VF_WAVES * t, t < nsl
     const int n16 = (L + VF_SLAB - 1) / VF_SLAB;
-    const int lo = (int)((int64_t)s * n16 / P.splits);
-    const int hi = (int)((int64_t)(s + 1) * n16 / P.splits);
+    // (wave-uniform values made explicitly scalar: derived through divisions,
+    // the compiler otherwise wraps the copies in loops over lanes)
+    const int lo = __builtin_amdgcn_readfirstlane((int)((int64_t)s * n16 / P.splits));
+    const int hi = __builtin_amdgcn_readfirstlane((int)((int64_t)(s + 1) * n16 / P.splits));
     const int nsl = hi - lo > wave ? (hi - lo - wave + VF_WAVES - 1) / VF_WAVES : 0;
     auto slab_k0 = [&](int t) { return (lo + wave + VF_WAVES * t) * VF_SLAB; };
 
@@ -340,10 +342,7 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
         int id = 0;
         if constexpr (FAST) {
             const int u = u0 + lane;
-            if (u < nsl) {
-                id = P.bt[bt_row + (int)fdiv((uint32_t)slab_k0(u), fd)];
-                id = (uint32_t)id < nb32 ? id : 0;   // an id outside the pool reads block 0 (caller error)
-            }
+            if (u < nsl) id = P.bt[bt_row + (int)fdiv((uint32_t)slab_k0(u), fd)];
         }
         return id;
     };
@@ -354,7 +353,8 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
             tb = u;
             blkv = load_blocks(u);
         }
-        return __builtin_amdgcn_readlane(blkv, u - tb);
+        const int id = __builtin_amdgcn_readlane(blkv, u - tb);
+        return (uint32_t)id < nb32 ? id : 0;   // an id outside the pool reads block 0 (caller error)
     };
     // slab t into ring stage t % NSTAGE.  Rows past the context re-read the
     // context's last row: finite data whose P is 0.
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
         const int nv = min(VF_SLAB, L - k0);
         if constexpr (FAST) {
             const int bi = (int)fdiv((uint32_t)k0, fd);
-            const int kin = k0 - bi * P.block_size;
+            const int kin = __builtin_amdgcn_readfirstlane(k0 - bi * P.block_size);
             const uint32_t soff = (uint32_t)kin * stb32;
             const auto rk = vf_rsrc((const char *)P.k + (int64_t)blk * sbb + shb);
             const auto rv = vf_rsrc((const char *)P.v + (int64_t)blk * sbb + shb);
@@ -446,36 +446,32 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
-    // The Q^T operand (registers) and the block ids (loaded above) land in one
-    // round trip; the ring's copies follow.  The explicit wait lets the
-    // compiler's wait tracking know Q has landed: left pending, it would wait
-    // for every copy in flight before the loop's first MFMA on each iteration.
+    // The block ids (loaded above) and then the Q^T operand (registers) go out
+    // together.  The ring's copies wait only for the block ids: the Q loads,
+    // always exactly 2 NSTEP instructions issued after them, may stay in
+    // flight (the first slab's wait below covers them).
+    __builtin_amdgcn_sched_barrier(0);
     // ---- the lane's two S columns (16x16 blocks b = 0, 1): Q^T operand and
-    // the last key each column sees (-1: a padding column past the chunk)
+    // the last key each column sees (-1: a padding column past the chunk,
+    // which computes on a copy of the chunk's last column; it is never written)
     int lim[2];
     bf16x8 qf[2][NSTEP];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int col = c * VF_COLS + 16 * b + (lane & 15);
-        if (col < ncol) {
-            const int row = col / P.group, hq = g * P.group + col % P.group;
-            lim[b] = P.causal ? L - Lq + row : L - 1;
-            const __bf16 *qp = (const __bf16 *)P.q + ((int64_t)(q0 + row) * P.Hq + hq) * D + 8 * (lane >> 4);
+        const int cc = min(col, ncol - 1);
+        const int row = cc / P.group, hq = g * P.group + cc % P.group;
+        lim[b] = col < ncol ? (P.causal ? L - Lq + row : L - 1) : -1;
+        const __bf16 *qp = (const __bf16 *)P.q + ((int64_t)(q0 + row) * P.Hq + hq) * D + 8 * (lane >> 4);
 #pragma unroll
-            for (int st = 0; st < NSTEP; ++st) qf[b][st] = *(const bf16x8 *)(qp + 32 * st);
-        } else {
-            lim[b] = -1;
-#pragma unroll
-            for (int st = 0; st < NSTEP; ++st) qf[b][st] = bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
-        }
+        for (int st = 0; st < NSTEP; ++st) qf[b][st] = *(const bf16x8 *)(qp + 32 * st);
     }
-    // a slab needs masking once its last key passes the first real column's limit
-    const int min_lim = P.causal ? L - Lq + (c * VF_COLS) / P.group : L - 1;
-
-    vf_wait_copies<0>();
+    vf_wait_copies<2 * NSTEP>();   // the block ids have landed
 #pragma unroll
     for (int t = 0; t < C::NSTAGE; ++t)
         if (t < nsl) issue(t, FAST ? slab_block(t) : 0);
+    // a slab needs masking once its last key passes the first real column's limit
+    const int min_lim = P.causal ? L - Lq + (c * VF_COLS) / P.group : L - 1;
 
     auto stage = [&](int t) -> const char * { return ring + (t % C::NSTAGE) * C::STAGE; };
     // S^T = K Q^T of the slab in stage stg: acc[b][i] = S(key 4 (lane >> 4) + i,
