@@ -7,9 +7,9 @@
 //
 // Work item: (request, KV head, column tile, key split).  A column tile holds
 // 32 (chunk row, q head of the KV head's group) pairs, rows major.  The split's
-// keys are cut into slabs of 16; wave w of the workgroup's 4 takes slabs
-// w, w + 4, w + 8, ... of the range, so the waves split the keys and every wave
-// computes all 32 columns.  Each wave streams its slabs' K and V rows straight
+// keys are cut into slabs of 16; wave w of the workgroup's NW = 4 takes slabs
+// w, w + NW, w + 2 NW, ... of the range, so the waves split the keys and every
+// wave computes all 32 columns.  Each wave streams its slabs' K and V rows straight
 // from the pool into a ring of its own in LDS (direct global-to-LDS copies; no
 // tile images and no workgroup barrier inside the loop), and per slab
 //   - S^T = K Q^T on 16x16x32 bf16 MFMAs (K rows as the A operand, Q^T pinned
@@ -18,7 +18,7 @@
 //   - O^T += V^T P^T on 32x32x16 bf16 MFMAs, the V^T operand read from the
 //     row-major V rows with gfx950's transposing LDS reads (ds_read_b64_tr_b16,
 //     or ds_read_b64_tr_b8 for int8 codes).
-// The 4 waves' (maximum, sum, O) merge in LDS at the end; the item writes its
+// The waves' (maximum, sum, O) merge in LDS at the end; the item writes its
 // range's normalised O and log-sum-exp (or, with one split, the output).
 //
 // int8 pools: the codes are read as codes (one byte per element) and become
@@ -43,7 +43,7 @@
 namespace pa {
 namespace {
 
-constexpr int VF_WAVES = 4;        // waves per workgroup
+constexpr int VF_MAX_WAVES = 4;    // waves per workgroup, at most
 constexpr int VF_SLAB = 16;        // keys per wave step
 constexpr int VF_COLS = 32;        // columns per work item
 constexpr float VF_PSHIFT = 40.f;  // P = 2^(x - m - VF_PSHIFT)
@@ -63,12 +63,15 @@ struct VfCfg {
     static constexpr int NCOPY = SLAB_BYTES / 1024;     // 1 KB copies per K (or V) slab
     static constexpr int SCL = I8 ? 256 : 0;            // one scale copy: 64 lanes x 4 bytes
     static constexpr int STAGE = 2 * SLAB_BYTES + 2 * SCL;
+    // (3 waves of 3 stages for bf16 at D 256, two slabs in flight per wave in
+    // place of one, measured the same: 51.8 us at 60k either way)
+    static constexpr int NW = 4;                                     // waves per workgroup
     static constexpr int NSTAGE = (!I8 && D == 256) ? 2 : 4;
     static constexpr int COPIES = 2 * NCOPY + (I8 ? 2 : 0);   // copy instructions per slab
-    static constexpr int RING = VF_WAVES * NSTAGE * STAGE;
+    static constexpr int RING = NW * NSTAGE * STAGE;
     static constexpr int MROW = D * 4 + 16;             // merge area: one column's fp32 row, padded
-    static constexpr int MERGE = VF_WAVES * VF_COLS * MROW;
-    static constexpr int HDR = (2 * VF_WAVES + 2) * VF_COLS * 4;
+    static constexpr int MERGE = NW * VF_COLS * MROW;
+    static constexpr int HDR = (2 * NW + 2) * VF_COLS * 4;
     static constexpr int BODY = RING > MERGE ? RING : MERGE;
     static constexpr int LDS = BODY + HDR;
     static_assert(NCOPY >= 1 && RPC * RB == 1024, "copy shape");
@@ -280,7 +283,7 @@ __device__ __forceinline__ float vf_sum16(float x) {
 }
 
 template <int D, bool I8, bool FAST>
-__global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyParams P) {
+__global__ __launch_bounds__(VF_MAX_WAVES * 64, 1) void verify_kernel(const VerifyParams P) {
     using C = VfCfg<D, I8>;
     constexpr int NSTEP = D / 32;   // QK k-steps and PV dim blocks
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -304,14 +307,14 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
     const int ncol = Lq * P.group;
     if (c * VF_COLS >= ncol) return;
 
-    // ---- this wave's slabs: lo + wave + VF_WAVES * t, t < nsl
+    // ---- this wave's slabs: lo + wave + NW * t, t < nsl
     const int n16 = (L + VF_SLAB - 1) / VF_SLAB;
     // (wave-uniform values made explicitly scalar: derived through divisions,
     // the compiler otherwise wraps the copies in loops over lanes)
     const int lo = __builtin_amdgcn_readfirstlane((int)((int64_t)s * n16 / P.splits));
     const int hi = __builtin_amdgcn_readfirstlane((int)((int64_t)(s + 1) * n16 / P.splits));
-    const int nsl = hi - lo > wave ? (hi - lo - wave + VF_WAVES - 1) / VF_WAVES : 0;
-    auto slab_k0 = [&](int t) { return (lo + wave + VF_WAVES * t) * VF_SLAB; };
+    const int nsl = hi - lo > wave ? (hi - lo - wave + C::NW - 1) / C::NW : 0;
+    auto slab_k0 = [&](int t) { return (lo + wave + C::NW * t) * VF_SLAB; };
 
     char *ring = smem + wave * C::NSTAGE * C::STAGE;
     const int64_t stb = P.stride_tok * C::EB, sbb = P.stride_block * C::EB;
@@ -677,11 +680,11 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
         for (int b = 0; b < 2; ++b) sacc[b] = snext[b];
     }
 
-    // ---- merge of the 4 waves
+    // ---- merge of the waves
     __syncthreads();   // every wave is out of its ring (the merge area overlaps the rings)
     float *hm = (float *)(smem + C::BODY);          // [wave][32] reference maxima
-    float *hl = hm + VF_WAVES * VF_COLS;            // [wave][32] sums
-    float *hM = hl + VF_WAVES * VF_COLS;            // [32] merged maxima
+    float *hl = hm + C::NW * VF_COLS;               // [wave][32] sums
+    float *hM = hl + C::NW * VF_COLS;               // [32] merged maxima
     float *hL = hM + VF_COLS;                       // [32] merged sums
 #pragma unroll
     for (int b = 0; b < 2; ++b) l_run[b] = sum_halves(vf_sum16(l_run[b]));
@@ -695,10 +698,10 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
     const int oc = lane & 31;   // the O column of this lane
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < VF_WAVES; ++w) M = fmaxf(M, hm[w * VF_COLS + oc]);
+    for (int w = 0; w < C::NW; ++w) M = fmaxf(M, hm[w * VF_COLS + oc]);
     float Lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < VF_WAVES; ++w) {
+    for (int w = 0; w < C::NW; ++w) {
         const float mw = hm[w * VF_COLS + oc];
         Lt += mw == -INFINITY ? 0.f : exp2_fast(mw - M) * hl[w * VF_COLS + oc];
     }
@@ -722,14 +725,14 @@ __global__ __launch_bounds__(VF_WAVES * 64, 1) void verify_kernel(const VerifyPa
 
     // ---- output: the range's normalised O and log-sum-exp, or the result
     constexpr int D4 = D / 4;
-    for (int idx = threadIdx.x; idx < VF_COLS * D4; idx += VF_WAVES * 64) {
+    for (int idx = threadIdx.x; idx < VF_COLS * D4; idx += C::NW * 64) {
         const int cl = idx / D4, d4 = idx % D4;
         const int col = c * VF_COLS + cl;
         if (col >= ncol) continue;
         const int row = col / P.group, hq = g * P.group + col % P.group;
         f32x4 sum = *(const f32x4 *)(smem + cl * C::MROW + 16 * d4);
 #pragma unroll
-        for (int w = 1; w < VF_WAVES; ++w) sum += *(const f32x4 *)(smem + (w * VF_COLS + cl) * C::MROW + 16 * d4);
+        for (int w = 1; w < C::NW; ++w) sum += *(const f32x4 *)(smem + (w * VF_COLS + cl) * C::MROW + 16 * d4);
         const int64_t ph = (int64_t)(q0 + row) * P.Hq + hq;
         if (P.o_part) {
             const int64_t pp = ((int64_t)r * P.max_q + row) * P.Hq + hq;   // partial row
@@ -824,9 +827,9 @@ __global__ __launch_bounds__(VM_THREADS) void verify_merge_kernel(const VerifyPa
 template <int D, bool I8>
 hipError_t launch_verify_d(const VerifyParams &p, dim3 grid, hipStream_t stream) {
     if (p.block_size % VF_SLAB == 0)
-        hipLaunchKernelGGL((verify_kernel<D, I8, true>), grid, dim3(VF_WAVES * 64), 0, stream, p);
+        hipLaunchKernelGGL((verify_kernel<D, I8, true>), grid, dim3(VfCfg<D, I8>::NW * 64), 0, stream, p);
     else
-        hipLaunchKernelGGL((verify_kernel<D, I8, false>), grid, dim3(VF_WAVES * 64), 0, stream, p);
+        hipLaunchKernelGGL((verify_kernel<D, I8, false>), grid, dim3(VfCfg<D, I8>::NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
