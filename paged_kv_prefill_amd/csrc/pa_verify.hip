@@ -758,9 +758,9 @@ __global__ __launch_bounds__(VF_MAX_WAVES * 64, 1) void verify_kernel(const Veri
     }
 }
 
-// Merge of the split partials (deterministic: the splits are summed in
-// order), as the split-KV merge of the prefill entries but over partials
-// indexed by (request, chunk row), which lets every load go out at once: one
+// Merge of the split partials (deterministic: a fixed summation order), as
+// the split-KV merge of the prefill entries but over partials indexed by
+// (request, chunk row), which lets every load go out at once: one
 // wave per (request, chunk row, q head, 64 output elements), one element per
 // lane:  m = max_s lse_s,  w_s = e^{lse_s - m} (0 for an empty split),
 //        O = sum_s w_s O_s / sum_s w_s,  lse = m + ln sum_s w_s.
@@ -799,9 +799,13 @@ __global__ __launch_bounds__(VM_THREADS) void verify_merge_kernel(const VerifyPa
     for (int s = lane + 64; s < P.splits; s += 64) m = fmaxf(m, ls[s]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    float acc = 0.f;
-    float wsum = 0.f;
-    // split s0 + j's weight is computed by lane j and read by every lane
+    // split s0 + j's weight is computed by lane j and read by every lane.  The
+    // verify kernel writes every split's partial (zeros where a row sees none
+    // of its keys), so a split of weight 0 adds 0 and needs no branch; the
+    // splits are summed in four interleaved chains (split j into chain j mod
+    // 4, the chains added in order at the end), a fixed order.
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float wsum[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < P.splits; s0 += VM_BATCH) {
         if (s0 > 0) {
 #pragma unroll
@@ -811,17 +815,18 @@ __global__ __launch_bounds__(VM_THREADS) void verify_merge_kernel(const VerifyPa
         const float wj = lj == -INFINITY ? 0.f : expf(lj - m);
 #pragma unroll
         for (int j = 0; j < VM_BATCH; ++j) {
-            if (__builtin_amdgcn_readlane(__float_as_int(lj), j) == __float_as_int(-INFINITY)) continue;
             const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
-            wsum += w;
-            acc += w * o[j];
+            wsum[j & 3] += w;
+            acc[j & 3] = fmaf(w, o[j], acc[j & 3]);
         }
     }
+    const float accs = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float ws = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
     const int64_t ph = (int64_t)(q0 + i) * P.Hq + h;
-    const float inv = 1.0f / wsum;
-    if constexpr (OUT_BF16) ((__bf16 *)P.out)[ph * D + e0] = (__bf16)(acc * inv);
-    else ((float *)P.out)[ph * D + e0] = acc * inv;
-    if (P.lse && e0 == 0) P.lse[ph] = m + logf(wsum);
+    const float inv = 1.0f / ws;
+    if constexpr (OUT_BF16) ((__bf16 *)P.out)[ph * D + e0] = (__bf16)(accs * inv);
+    else ((float *)P.out)[ph * D + e0] = accs * inv;
+    if (P.lse && e0 == 0) P.lse[ph] = m + logf(ws);
 }
 
 template <int D, bool I8>
