@@ -681,9 +681,13 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // kin: the first PFQ K operands of tile kt+1, read by the previous step;
     // kout: the same for tile kt+2, read here in phase B
     auto step = [&](int kt, int cur, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&kin)[PFQ],
-                    u32x4 (&kout)[PFQ], auto has_next, auto mask_next) PA_INL {
+                    u32x4 (&kout)[PFQ], auto has_next, auto mask_next, auto v_ranged) PA_INL {
         constexpr bool NEXT = decltype(has_next)::value;
         constexpr bool MASK = decltype(mask_next)::value;
+        // VR: some V tile of this workgroup's key range may be scaled (vr_any);
+        // the unmasked steps are compiled both ways, so the common loop holds no
+        // branch for the range factors
+        constexpr bool VR = decltype(v_ranged)::value;
         constexpr int N0 = NEXT ? NPA : 0;             // PV MFMAs issued in phase A
         constexpr int NB = NP - N0;                    // phase-B slots
         const char *kl = kstage(cur ^ 1);
@@ -712,7 +716,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         f32x4 ksc[2][4];
         // V(kt)'s range factor, before any read of its operands (only where
         // some tile of this workgroup's range is scaled)
-        if (__builtin_expect(vr_any, 0)) {
+        if (VR && __builtin_expect(vr_any, 0)) {
             const uint32_t vf = __builtin_amdgcn_readfirstlane(*(const uint32_t *)(vl + VT_FACTOR_OFF));
             if (vf != vcur) v_range(vf, cur);
         }
@@ -843,9 +847,16 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // steps whose next tile is unmasked, two at a time (stages 0 then 1)
     const int end1 = min(t_mask, kt_end) - 1;
     int kt = kt_begin;
-    for (; kt + 1 < end1; kt += 2) {
-        step(kt, 0, sa, sb, ka0, ka1, yes{}, no{});
-        step(kt + 1, 1, sb, sa, ka1, ka0, yes{}, no{});
+    if (__builtin_expect(vr_any, 0)) {
+        for (; kt + 1 < end1; kt += 2) {
+            step(kt, 0, sa, sb, ka0, ka1, yes{}, no{}, yes{});
+            step(kt + 1, 1, sb, sa, ka1, ka0, yes{}, no{}, yes{});
+        }
+    } else {
+        for (; kt + 1 < end1; kt += 2) {
+            step(kt, 0, sa, sb, ka0, ka1, yes{}, no{}, no{});
+            step(kt + 1, 1, sb, sa, ka1, ka0, yes{}, no{}, no{});
+        }
     }
     auto roll = [&]() PA_INL {
 #pragma unroll
@@ -854,16 +865,16 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         for (int m = 0; m < PFQ; ++m) ka0[m] = ka1[m];
     };
     if (kt < end1) {
-        step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, yes{}, no{});
+        step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, yes{}, no{}, yes{});
         ++kt;
         roll();
     }
     // steps whose next tile is masked (the last one or two)
     for (; kt + 1 < kt_end; ++kt) {
-        step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, yes{}, yes{});
+        step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, yes{}, yes{}, yes{});
         roll();
     }
-    step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, no{}, no{});
+    step(kt, (kt - kt_begin) & 1, sa, sb, ka0, ka1, no{}, no{}, yes{});
     // copies still in flight (the last steps re-copy into stages nobody reads)
     // land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
