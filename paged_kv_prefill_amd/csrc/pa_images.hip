@@ -65,6 +65,24 @@ __device__ __forceinline__ float fp8_at(uint32_t word, int b) {
     return (b >> 1) ? hi[b & 1] : lo[b & 1];
 }
 
+// The V^T tile is staged in LDS as its D rows of 64 fp16 columns (128 bytes,
+// no padding), the 8-byte groups (4 columns) permuted so that one store
+// instruction of a wave spreads over all banks.  The units of one store hold
+// dims d = 8 dc + e (bf16) or 16 dc + e (int8, fp8) for 32 or 16 chunks dc,
+// a multiple of 1,024 bytes apart, i.e. on one bank offset.  Group gi of row d
+// goes to group gi ^ ((d >> 4) & 15), and rows d and d ^ 1 trade the group
+// pairs where ((d >> 3) ^ (gi >> 1)) is odd, which puts the 32 (bf16) or the
+// 2 x 16 (int8: units of odd and even position groups) stores of a half-wave in
+// distinct banks.  The copy-out undoes it and adds each row's padding, and the
+// scales go to HBM straight from the registers, so the staging is exactly 32 KB
+// at head_dim 256 and five workgroups fit on a CU (a 2,048-token chunk's
+// 1,252 tiles at once).
+constexpr int VS_ROW = TILE_KEYS * 2;   // bytes per staged V^T row
+__device__ __forceinline__ int vt_stage_off(int d, int slot) {
+    const int gi = slot >> 2;
+    return (d ^ (((d >> 3) ^ (gi >> 1)) & 1)) * VS_ROW + (((gi ^ (d >> 4)) & 15) << 3);
+}
+
 // V^T image: [D][72] fp16 (64 columns in MFMA-position order + zero padding,
 // the tile's range factor 2^e in row 0's padding) + 64 scales in position
 // order.  One unit = 4 consecutive positions (4 consecutive columns) x one
@@ -81,14 +99,15 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
     constexpr int UNITS = 16 * CPR;
     constexpr int NU = (UNITS + IT - 1) / IT;  // units per thread
     constexpr int V_BYTES = vt_tile_bytes(D);
-    __shared__ __attribute__((aligned(16))) char img[V_BYTES + TILE_KEYS * 4];
-    __shared__ float wave_amax[IT / 64];
+    // the staged tile; its first IT / 64 words first carry the waves' maxima
+    __shared__ __attribute__((aligned(16))) char img[D * VS_ROW];
+    float *wave_amax = (float *)img;
     int t, g, r, L;
     if (!img_tile(P, t, g, r, L)) return;
     const int tid = threadIdx.x;
     const int rpi = P.v_rpi;
-    float *scl = (float *)(img + V_BYTES);
-    for (int d = tid; d < D; d += IT) *(u32x4 *)(img + d * VT_ROW_BYTES + TILE_KEYS * 2) = u32x4{0, 0, 0, 0};
+    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * v_image_bytes(D);
+    float *scl = (float *)(dst + V_BYTES);
     float x[NU][4][EPC];
     float amax = 0.f;
 #pragma unroll
@@ -126,6 +145,7 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < IT / 64; ++w) amax = fmaxf(amax, wave_amax[w]);
+    __syncthreads();   // every wave has read the maxima before the tile overwrites them
     const int e_range = vt_range_exp(__float_as_uint(amax));
     const float down = __uint_as_float((uint32_t)(127 - e_range) << 23);   // 2^-e, exact
 #pragma unroll
@@ -136,15 +156,32 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
         const int slot = vt_slot(pg * 4);
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
-            *(u32x2 *)(img + vt_off(dc * EPC + e, slot)) =
+            *(u32x2 *)(img + vt_stage_off(dc * EPC + e, slot)) =
                 u32x2{pack_f16x2(x[ui][0][e] * down, x[ui][1][e] * down),
                       pack_f16x2(x[ui][2][e] * down, x[ui][3][e] * down)};
     }
-    if (tid == 0) *(float *)(img + VT_FACTOR_OFF) = __uint_as_float((uint32_t)(127 + e_range) << 23);
     __syncthreads();
-    char *dst = (char *)P.dst + (((int64_t)r * P.tiles + t) * P.Hkv + g) * v_image_bytes(D);
-    constexpr int CHUNKS = (V_BYTES + TILE_KEYS * 4) / 16;
-    for (int c = tid; c < CHUNKS; c += IT) *(u32x4 *)(dst + c * 16) = *(const u32x4 *)(img + c * 16);
+    // the image's rows: 8 chunks of columns and a padding chunk each (zeros; row
+    // 0's holds the range factor 2^e)
+    constexpr int RCH = VT_ROW_BYTES / 16;
+    static_assert(RCH == 9 && VT_FACTOR_OFF == 8 * 16, "a V^T row is 8 column chunks + 16 bytes");
+    const uint32_t factor = (uint32_t)(127 + e_range) << 23;
+    for (int c = tid; c < D * RCH; c += IT) {
+        const int d = c / RCH, k = c % RCH;
+        u32x4 w;
+        if (k < RCH - 1) {
+            // columns 8k .. 8k + 7 are groups 2k and 2k + 1: both in row
+            // d ^ (((d >> 3) ^ k) & 1), as its 16-byte pair k ^ (sw >> 1), in
+            // swapped order where sw is odd
+            const int sw = (d >> 4) & 15;
+            const int row = d ^ (((d >> 3) ^ k) & 1);
+            w = *(const u32x4 *)(img + row * VS_ROW + ((k ^ (sw >> 1)) << 4));
+            if (sw & 1) w = u32x4{w[2], w[3], w[0], w[1]};
+        } else {
+            w = u32x4{d == 0 ? factor : 0u, 0u, 0u, 0u};
+        }
+        *(u32x4 *)(dst + c * 16) = w;
+    }
 }
 
 // K image of an int8 pool: [64][D] bf16 codes (exact) in key order + 64
