@@ -367,9 +367,9 @@ int pa_prefill_int8qk(const pa_paged_args *args, const void *q, const int8_t *k8
 /*
  * pa_workspace_bytes -- device workspace an attention entry point needs for
  * these arguments: n = num_reqs * ceil(max_ctx_len / 64) * num_kv_heads V tile
- * images of 144 * head_dim + 256 bytes (fp16 rows of 64 keys padded to 72, the
- * tile's power-of-two range factor in the padding of its first row, plus
- * scales), and for PA_ENTRY_PREFILL_INT8KV / _FP8KV n more K tile images of
+ * images of 128 * head_dim + 272 bytes (fp16 rows of 64 keys, 64 scales, and
+ * a 16-byte word holding the tile's power-of-two range factor), and for
+ * PA_ENTRY_PREFILL_INT8KV / _FP8KV n more K tile images of
  * 128 * head_dim + 256 bytes; then, from the next multiple of 256 bytes, the
  * work schedule: 4 bytes per attention workgroup, num_reqs * num_kv_heads *
  * ceil(max_q_len * (num_q_heads / num_kv_heads) / 128) rounded up to a

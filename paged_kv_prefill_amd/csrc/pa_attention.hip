@@ -461,7 +461,11 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 
     // per-lane operand read bases: K row of MFMA position 32 kb + lc, V^T row lc
     const int k_rd = K_COPY_STRIDE * (lc % C::KCOPIES) + (lc / C::KCOPIES) * C::K_ROW_BYTES + hf * 16;
-    const int v_rd = lc * VT_ROW_BYTES + hf * 16;
+    // V^T row lc; its 16-byte chunk for key step k (keys 16k + 8 hf ..) is stored at
+    // position (2k + hf) ^ vt_chunk_swz(lc), the same for every block of 32 rows
+    int v_rd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v_rd[k] = lc * VT_ROW_BYTES + (((2 * k + hf) ^ vt_chunk_swz(lc)) << 4);
 
     // ---- S^T = K Q^T for the 2 blocks of 32 keys of a K stage (raw logits, the
     // int8-QK arm's times the key scale); A operands are read two
@@ -634,7 +638,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     bool scaled = false;   // (read while the first tiles' copies are in flight)
     for (int kt = kt_begin + tid; kt < kt_end; kt += NTHR)
         scaled |= *(const uint32_t *)(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D) +
-                                      VT_FACTOR_OFF) != 0x3f800000u;
+                                      vt_factor_off(D)) != 0x3f800000u;
     uint32_t *flags = (uint32_t *)(smem + C::FLAG_OFF);
     const bool wave_scaled = __any(scaled);
     if (lane == 0) flags[wave] = wave_scaled ? 1u : 0u;
@@ -674,7 +678,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         return *(const u32x4 *)(kr + (m & 1) * C::KB_STEP + (m >> 1) * 32);
     };
     auto rdV = [&](const char *vr, int n) PA_INL -> f16x8 {   // V^T operand of PV MFMA n
-        return *(const f16x8 *)(vr + (n % C::DB) * 32 * VT_ROW_BYTES + (n / C::DB) * 32);
+        return *(const f16x8 *)(vr + v_rd[n / C::DB] + (n % C::DB) * 32 * VT_ROW_BYTES);
     };
 
     // HAS_NEXT: tile kt+1 exists; MASK_NEXT: it needs masking
@@ -693,7 +697,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         const char *kl = kstage(cur ^ 1);
         const char *kr = kl + k_rd;
         const char *vl = vstage(cur);
-        const char *vr = vl + v_rd;
+        const char *vr = vl;
         // copies: V(kt+1) during phase A (its stage held V(kt-1), done before the
         // previous step's last barrier), K(kt+3) during phase B (its stage holds
         // K(kt+1), done once every wave is past phase A), spread evenly over the
@@ -717,7 +721,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
         // V(kt)'s range factor, before any read of its operands (only where
         // some tile of this workgroup's range is scaled)
         if (VR && __builtin_expect(vr_any, 0)) {
-            const uint32_t vf = __builtin_amdgcn_readfirstlane(*(const uint32_t *)(vl + VT_FACTOR_OFF));
+            const uint32_t vf = __builtin_amdgcn_readfirstlane(
+                *(const uint32_t *)(P.v_img + (img_base + (int64_t)kt * P.Hkv) * v_image_bytes(D) + vt_factor_off(D)));
             if (vf != vcur) v_range(vf, cur);
         }
 #pragma unroll

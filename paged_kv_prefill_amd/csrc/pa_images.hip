@@ -73,19 +73,20 @@ __device__ __forceinline__ float fp8_at(uint32_t word, int b) {
 // goes to group gi ^ ((d >> 4) & 15), and rows d and d ^ 1 trade the group
 // pairs where ((d >> 3) ^ (gi >> 1)) is odd, which puts the 32 (bf16) or the
 // 2 x 16 (int8: units of odd and even position groups) stores of a half-wave in
-// distinct banks.  The copy-out undoes it and adds each row's padding, and the
+// distinct banks.  The copy-out undoes it, and the
 // scales go to HBM straight from the registers, so the staging is exactly 32 KB
 // at head_dim 256 and five workgroups fit on a CU (a 2,048-token chunk's
-// 1,252 tiles at once).
+// 1,252 tiles at once).  (The image's own chunk order, vt_chunk_swz, is the
+// attention kernel's LDS layout and is applied at the copy-out.)
 constexpr int VS_ROW = TILE_KEYS * 2;   // bytes per staged V^T row
 __device__ __forceinline__ int vt_stage_off(int d, int slot) {
     const int gi = slot >> 2;
     return (d ^ (((d >> 3) ^ (gi >> 1)) & 1)) * VS_ROW + (((gi ^ (d >> 4)) & 15) << 3);
 }
 
-// V^T image: [D][72] fp16 (64 columns in MFMA-position order + zero padding,
-// the tile's range factor 2^e in row 0's padding) + 64 scales in position
-// order.  One unit = 4 consecutive positions (4 consecutive columns) x one
+// V^T image: [D][64] fp16 (64 columns in MFMA-position order, 16-byte chunks
+// permuted per row) + 64 scales in position order + the tile's range factor
+// 2^e.  One unit = 4 consecutive positions (4 consecutive columns) x one
 // 16-byte chunk of the source row; its 4 x 8 (bf16) or 4 x 16 (int8, fp8)
 // values go to LDS as 8-byte groups of the 4 columns of one dim.  The values
 // are read first (all of a thread's units), the tile's largest magnitude is
@@ -161,27 +162,20 @@ __global__ __launch_bounds__(IT) void v_image_kernel(const ImageParams P) {
                       pack_f16x2(x[ui][2][e] * down, x[ui][3][e] * down)};
     }
     __syncthreads();
-    // the image's rows: 8 chunks of columns and a padding chunk each (zeros; row
-    // 0's holds the range factor 2^e)
-    constexpr int RCH = VT_ROW_BYTES / 16;
-    static_assert(RCH == 9 && VT_FACTOR_OFF == 8 * 16, "a V^T row is 8 column chunks + 16 bytes");
-    const uint32_t factor = (uint32_t)(127 + e_range) << 23;
-    for (int c = tid; c < D * RCH; c += IT) {
-        const int d = c / RCH, k = c % RCH;
-        u32x4 w;
-        if (k < RCH - 1) {
-            // columns 8k .. 8k + 7 are groups 2k and 2k + 1: both in row
-            // d ^ (((d >> 3) ^ k) & 1), as its 16-byte pair k ^ (sw >> 1), in
-            // swapped order where sw is odd
-            const int sw = (d >> 4) & 15;
-            const int row = d ^ (((d >> 3) ^ k) & 1);
-            w = *(const u32x4 *)(img + row * VS_ROW + ((k ^ (sw >> 1)) << 4));
-            if (sw & 1) w = u32x4{w[2], w[3], w[0], w[1]};
-        } else {
-            w = u32x4{d == 0 ? factor : 0u, 0u, 0u, 0u};
-        }
+    // the image: chunk pos of row d holds the row's columns 8k .. 8k + 7, k =
+    // pos ^ vt_chunk_swz(d) (groups 2k and 2k + 1 of the staging: both in row
+    // d ^ (((d >> 3) ^ k) & 1), as its 16-byte pair k ^ (sw >> 1), in swapped
+    // order where sw is odd); then the factor word
+    static_assert(VT_ROW_BYTES == 8 * 16, "a V^T row is 8 chunks");
+    for (int c = tid; c < D * 8; c += IT) {
+        const int d = c >> 3, k = (c & 7) ^ vt_chunk_swz(d);
+        const int sw = (d >> 4) & 15;
+        const int row = d ^ (((d >> 3) ^ k) & 1);
+        u32x4 w = *(const u32x4 *)(img + row * VS_ROW + ((k ^ (sw >> 1)) << 4));
+        if (sw & 1) w = u32x4{w[2], w[3], w[0], w[1]};
         *(u32x4 *)(dst + c * 16) = w;
     }
+    if (tid == 0) *(u32x4 *)(dst + vt_factor_off(D)) = u32x4{(uint32_t)(127 + e_range) << 23, 0u, 0u, 0u};
 }
 
 // K image of an int8 pool: [64][D] bf16 codes (exact) in key order + 64

@@ -12,36 +12,39 @@
 // lanes of one LDS read phase hit 16 different 4-bank groups and every operand
 // read of a lane is its own base plus a compile-time offset.
 //
-// V^T tile (fp16): [D][64 + 8 pad] (144-byte rows, 36 dwords: 16 consecutive
-// rows fall on 16 disjoint 4-bank groups).  Its 64 columns follow the MFMA
-// positions of the K tile (column of position p holds key tile_key(p)), with
-// positions {0-3, 8-11} of each group of 16 in columns 0-7 and {4-7, 12-15} in
-// columns 8-15: the order in which the S accumulator rows reach the PV MFMA,
-// so each PV operand is one 16-byte read.
+// V^T tile (fp16): [D][64] (128-byte rows, no padding).  Its 64 columns
+// follow the MFMA positions of the K tile (column of position p holds key
+// tile_key(p)), with positions {0-3, 8-11} of each group of 16 in columns 0-7
+// and {4-7, 12-15} in columns 8-15: the order in which the S accumulator rows
+// reach the PV MFMA, so each PV operand is one 16-byte read.  The eight
+// 16-byte chunks of row d are stored permuted, chunk c at c ^ vt_chunk_swz(d):
+// a PV operand read takes one chunk from each of 32 consecutive rows (two
+// chunks c, c ^ 1 per row over the wave), and rows a multiple of 128 bytes
+// apart would otherwise share their banks.  The permutation gives the 16
+// rows of a 16-lane read phase 16 different 4-bank groups, and also the 8
+// rows x 2 chunks of a phase that pairs lanes l and l + 32.
 //
 // fp16 tops out at 65504, so a tile holds V * 2^-e: e >= 0 is the smallest
 // power of two that brings the tile's largest |V| below 2^15 (0 for any tile
 // whose values are all below 2^15 in magnitude, or that holds an infinity;
 // NaNs take no part in the maximum).
-// The factor 2^e itself, as an fp32, sits in the padding of row 0 (byte
-// VT_FACTOR_OFF), which the PV operands never read, so it reaches LDS with the
-// tile's own copies.
 //
 // V^T images in global memory (the workspace) are byte-for-byte copies of the
-// LDS tile followed by 64 fp32 per-key scales in position order (int8 V), so
-// a workgroup moves them with straight 1 KB direct-to-LDS copies.  K images
-// (int8-KV exact arm) hold [64][D] bf16 codes in key order (the 1 KB copies
-// re-space them) followed by 64 fp32 per-key scales in key order.
+// LDS tile, followed by 64 fp32 per-key scales in position order (int8 V)
+// and a 16-byte word whose first fp32 is the tile's factor 2^e (read by the
+// attention kernel from memory, only where some tile of its key range has e >
+// 0), so a workgroup moves the tile with straight 1 KB direct-to-LDS copies.
+// K images (int8-KV exact arm) hold [64][D] bf16 codes in key order (the 1 KB
+// copies re-space them) followed by 64 fp32 per-key scales in key order.
 #pragma once
 #include <stdint.h>
 
 namespace pa {
 
 constexpr int TILE_KEYS = 64;
-constexpr int VT_ROW_BYTES = TILE_KEYS * 2 + 16;   // one padded V^T row (fp16)
+constexpr int VT_ROW_BYTES = TILE_KEYS * 2;        // one V^T row (fp16)
 
 constexpr int K_COPY_STRIDE = 1024 + 16;          // LDS bytes per 1 KB K copy
-constexpr int VT_FACTOR_OFF = TILE_KEYS * 2;      // fp32 2^e of a V^T tile: row 0's padding
 constexpr int VT_RANGE_LOG2 = 15;                 // a tile's |V| * 2^-e stays below 2^15
 
 // e of a V^T tile whose largest magnitude is amax (see above): from amax's
@@ -59,11 +62,15 @@ __host__ __device__ constexpr int tile_key(int p, int rpi) {
     return rpi * (i % g) + i / g + (32 / g) * kb;
 }
 
-// bytes of one V^T tile in LDS and of one V^T image (tile + 64 fp32 scales)
+// bytes of one V^T tile in LDS and of one V^T image (tile + 64 fp32 scales +
+// the factor word); the factor's byte offset in an image
 __host__ __device__ constexpr int vt_tile_bytes(int head_dim) { return head_dim * VT_ROW_BYTES; }
 __host__ __device__ constexpr int64_t v_image_bytes(int head_dim) {
-    return (int64_t)vt_tile_bytes(head_dim) + TILE_KEYS * 4;
+    return (int64_t)vt_tile_bytes(head_dim) + TILE_KEYS * 4 + 16;
 }
+__host__ __device__ constexpr int vt_factor_off(int head_dim) { return vt_tile_bytes(head_dim) + TILE_KEYS * 4; }
+// stored position of 16-byte chunk c of V^T row d is c ^ vt_chunk_swz(d)
+__host__ __device__ constexpr int vt_chunk_swz(int d) { return 2 * ((d >> 1) & 3) + ((d >> 3) & 1); }
 // bytes of one K image (int8-KV exact arm): 64 rows of bf16 codes + 64 scales
 __host__ __device__ constexpr int64_t k_image_bytes(int head_dim) {
     return (int64_t)TILE_KEYS * head_dim * 2 + TILE_KEYS * 4;
@@ -79,6 +86,8 @@ __host__ __device__ inline int vt_slot(int p) {
     return (p & ~15) | (k16 & 3) | ((k16 >> 3) << 2) | (((k16 >> 2) & 1) << 3);
 }
 // byte offset of (d, slot) in a V^T tile
-__host__ __device__ inline int vt_off(int d, int slot) { return d * VT_ROW_BYTES + slot * 2; }
+__host__ __device__ inline int vt_off(int d, int slot) {
+    return d * VT_ROW_BYTES + (((slot >> 3) ^ vt_chunk_swz(d)) << 4) + (slot & 7) * 2;
+}
 
 }  // namespace pa

@@ -291,7 +291,7 @@ def test_images_ready_flag(arm):
 def sched_offset(w, arm):
     """byte offset of the work schedule in an attention workspace"""
     n = len(w.ctx_lens) * -(-int(w.ctx_lens.max()) // 64) * w.num_kv_heads
-    img = n * (144 * w.head_dim + 256) + (n * (128 * w.head_dim + 256) if arm == "int8kv" else 0)
+    img = n * (128 * w.head_dim + 272) + (n * (128 * w.head_dim + 256) if arm == "int8kv" else 0)
     return -(-img // 256) * 256
 
 

@@ -97,7 +97,8 @@ def test_large_v_matches_oracle(orc, arm):
 
 def test_ordinary_v_unscaled_images():
     """Images of ordinary values carry the range factor 1 (e = 0) in the
-    padding word of their first row, which no PV operand reads."""
+    word after their 64 scales (byte 128 * D + 256 of each 128 * D + 272-byte
+    image)."""
     from paged_kv_prefill_amd import ops
     G = gc()
     w = synth.make_case(181, [40], [200], 16, 4, 2, 64)
@@ -106,7 +107,8 @@ def test_ordinary_v_unscaled_images():
     ws = ops.workspace(p, ops.PA_ENTRY_PREFILL_BF16)
     ops.pa_prefill_bf16(p, case.q, case.k_pool, case.v_pool, case.out(), ws=ws)
     torch.cuda.synchronize()
-    img = 144 * w.head_dim + 256
+    img = 128 * w.head_dim + 272
+    fo = 128 * w.head_dim + 256
     n = -(-200 // 64) * w.num_kv_heads
-    words = ws[:n * img].view(n, img)[:, 128:132].contiguous().view(torch.float32).cpu().numpy()
+    words = ws[:n * img].view(n, img)[:, fo:fo + 4].contiguous().view(torch.float32).cpu().numpy()
     assert np.all(words == 1.0)

@@ -263,8 +263,8 @@ def test_split_ranges_cover_every_tile_once(splits, t_full, n_tiles):
 
 
 def test_workspace_size_formula():
-    """num_reqs * ceil(max_ctx / 64) * Hkv V^T images of 144 * D + 256 bytes
-    (fp16 rows of 64 keys padded to 72), plus as many K images of 128 * D + 256
+    """num_reqs * ceil(max_ctx / 64) * Hkv V^T images of 128 * D + 272 bytes
+    (fp16 rows of 64 keys, 64 scales, a 16-byte factor word), plus as many K images of 128 * D + 256
     bytes for the int8-KV exact arm, then, from the next multiple of 256 bytes,
     the work schedule: one int32 per attention workgroup, num_reqs * Hkv *
     ceil(max_q_len * group / 128) rounded up to a multiple of 8."""
@@ -274,7 +274,7 @@ def test_workspace_size_formula():
                       (dict(num_reqs=5, max_ctx_len=300, max_q_len=100, num_kv_heads=2, head_dim=64),
                        5 * 2 * 2)]:
         a = _args(**kw)
-        vimg = 144 * 64 + 256
+        vimg = 128 * 64 + 272
         kimg = 128 * 64 + 256
         n = kw["num_reqs"] * -(-kw["max_ctx_len"] // 64) * 2
         sched = 4 * up(items, 8)
