@@ -163,7 +163,7 @@ int pa_prefill_bf16(const pa_paged_args *args, const void *q, const void *k_pool
  *     streams, other host threads) race.  Nothing in it needs clearing.
  *   - PA_ERR_TOO_LARGE if pa_workspace_bytes(args, PA_ENTRY_PREFILL_BF16)
  *     exceeds PA_NOALLOC_SCRATCH_BYTES (e.g. one request of head_dim 256 and 4
- *     KV heads up to a context of 28,864 tokens); nothing is enqueued.
+ *     KV heads up to a context of 32,448 tokens); nothing is enqueued.
  *   - PA_ERR_SHAPE if args->flags is not 0 (no call may rely on what an
  *     earlier one left in the shared array).
  *   - PA_ERR_LAUNCH if the array's device address cannot be found.

@@ -128,7 +128,7 @@ def test_noalloc_argument_errors():
     # whose workspace fits the array, and the next 64-key tile
     geo = dict(head_dim=256, num_kv_heads=4, num_q_heads=16, stride_head=256, stride_tok=1024,
                block_size=880, stride_block=880 * 1024, stride_bt=40, max_q_len=2048)
-    fits, over = _args(max_ctx_len=28864, **geo), _args(max_ctx_len=28865, **geo)
+    fits, over = _args(max_ctx_len=32448, **geo), _args(max_ctx_len=32449, **geo)
     assert L.pa_workspace_bytes(C.byref(fits), ops.PA_ENTRY_PREFILL_BF16) <= ops.PA_NOALLOC_SCRATCH_BYTES
     assert L.pa_workspace_bytes(C.byref(over), ops.PA_ENTRY_PREFILL_BF16) > ops.PA_NOALLOC_SCRATCH_BYTES
     assert L.pa_prefill_bf16_noalloc(C.byref(over), p, p, p, p, 0, None) == ops.PA_ERR_TOO_LARGE
