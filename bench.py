@@ -470,6 +470,36 @@ def arm_batched(steps, warmup):
                                "mfma_frac": fl / ms * 1e-9 / PEAK_BF16_TFLOPS}}
 
 
+def arm_kv_share(steps, warmup):
+    """One GPU's share of the headline when the KV heads are split over 4 GPUs:
+    KV head 0 with its 4 q heads (Hkv 1, Hq 4, same context and pool).  Its 64
+    column tiles fill a quarter of the CUs, so the split-KV entry point with 4
+    key splits (attention + merge) is timed beside the plain entry point
+    (whole calls, and the attention alone with the V images reused)."""
+    w = synth.config_bigpool_kv_share(0, 1)
+    P = Pools(w, w.extra["top_block_table"])
+    p = P.paged()
+    out = P.out()
+    ws = ops.workspace(p, ops.PA_ENTRY_PREFILL_BF16)
+    (t_call,), _ = time_launches([lambda: ops.pa_prefill_bf16(p, P.q, P.k, P.v, out, ws)], steps, warmup)
+    pr = P.paged()
+    pr.flags = ops.PA_FLAG_IMAGES_READY
+    S = 4
+    o_part, lse_part = ops.split_buffers(int(w.q_lens.sum()), w.num_q_heads, w.head_dim, S, DEV)
+    (t_plain, t_split), _ = time_launches(
+        [lambda: ops.pa_prefill_bf16(pr, P.q, P.k, P.v, out, ws),
+         lambda: ops.pa_prefill_bf16_splitkv(pr, P.q, P.k, P.v, out, S, o_part, lse_part, None, ws)],
+        steps, warmup)
+    fl = attn_flops(w)
+    chunk = int(w.q_lens.sum())
+    return {"kv_head_share_20k": {
+        "shape": "Hkv 1, Hq 4 (KV head 0 of the headline)", "splits": S,
+        "ms_call_plain": t_call, "tokens_per_s_plain": chunk / t_call * 1e3,
+        "ms_attention_plain": t_plain, "mfma_frac_plain": fl / t_plain * 1e-9 / PEAK_BF16_TFLOPS,
+        "ms_attention_split": t_split, "mfma_frac_split": fl / t_split * 1e-9 / PEAK_BF16_TFLOPS,
+        "note": "attention times with the V images reused; split = attention over 4 key ranges + merge"}}
+
+
 def arm_splitkv(steps, warmup):
     """Split-KV: (1) a short chunk (the bf16 workload's last 256 rows, 20,000
     context) whose 32 column tiles alone would leave most CUs idle, plain
@@ -691,6 +721,10 @@ def main():
         torch.cuda.empty_cache()
         arms.update(arm_splitkv(args.steps, args.warmup))
         progress("split-KV arms")
+        torch.cuda.empty_cache()
+        arms.update(arm_kv_share(args.steps, args.warmup))
+        progress("KV-head share arm")
+        torch.cuda.empty_cache()
         arms.update(arm_store(args.steps, args.warmup))
         progress("store arms")
         copy_gbs = measured_copy_gbs()

@@ -370,6 +370,21 @@ VERIFY_L = 60000
 VERIFY_Q = 8
 
 
+def config_bigpool_kv_share(g: int = 0, n_kv: int = 1) -> Workload:
+    """The bf16 big-pool workload cut to KV heads g .. g + n_kv - 1 and their q
+    heads (4 per KV head): the share one GPU holds when the KV heads are split
+    over 4 / n_kv GPUs.  Same values (seed 1), block size, pool size and
+    placements; the pool has n_kv KV heads."""
+    w = config_bigpool_bf16()
+    grp = w.num_q_heads // w.num_kv_heads
+    share = Workload(f"bigpool_bf16_kv{g}x{n_kv}", "bf16", w.q_lens, w.ctx_lens, w.block_size,
+                     w.num_blocks, n_kv * grp, n_kv, w.head_dim, w.block_table,
+                     np.ascontiguousarray(w.q[:, g * grp:(g + n_kv) * grp]),
+                     np.ascontiguousarray(w.k[:, g:g + n_kv]), np.ascontiguousarray(w.v[:, g:g + n_kv]))
+    share.extra["top_block_table"] = w.extra["top_block_table"]
+    return share
+
+
 def config_verify(kv_format: str = "int8") -> Workload:
     """Spec-decode verify: one request whose last 8 tokens (the drafted ones)
     attend to a 60,000-token context; block 880, 4 KV / 16 q heads, head_dim
