@@ -80,14 +80,11 @@ __host__ __device__ inline int64_t tiles_per_request(int32_t max_ctx_len) {
     return ((int64_t)max_ctx_len + TILE_KEYS - 1) / TILE_KEYS;
 }
 
-// column of MFMA position p (0..63) in a row of the V^T tile (swaps bits 2 and 3)
+// column of MFMA position p (0..63) in a row of the V^T tile, before the row's chunk
+// permutation (swaps bits 2 and 3)
 __host__ __device__ inline int vt_slot(int p) {
     const int k16 = p & 15;
     return (p & ~15) | (k16 & 3) | ((k16 >> 3) << 2) | (((k16 >> 2) & 1) << 3);
-}
-// byte offset of (d, slot) in a V^T tile
-__host__ __device__ inline int vt_off(int d, int slot) {
-    return d * VT_ROW_BYTES + (((slot >> 3) ^ vt_chunk_swz(d)) << 4) + (slot & 7) * 2;
 }
 
 }  // namespace pa
