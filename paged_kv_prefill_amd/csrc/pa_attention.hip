@@ -42,9 +42,9 @@
 // to LDS once and widened to 64 bits) plus a per-lane constant, and the loop
 // spends no vector instructions on addresses.  V comes from the per-tile V^T
 // images that pa_images.hip builds once per call.  The tile layouts
-// (pa_layout.h) pad rows instead of swizzling them, so every operand read of
-// a lane is one base register plus an immediate offset and no LDS read
-// conflicts.
+// (pa_layout.h: padded K rows, V^T rows with their 16-byte chunks permuted)
+// make every operand read of a lane a base register (one per key step for
+// V) plus an immediate offset, with no LDS read conflicts.
 //
 // Pipeline.  Step t runs, as a fixed program of slots separated by scheduling
 // fences, the QK MFMAs of tile t+1 beside tile t's exponentials (phase A) and
