@@ -817,7 +817,20 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             if constexpr (MASK)
                 if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) v = -INFINITY;
             sn[kb][i] = v;
-            mxa = fmaxf(mxa, v);
+            // the running maximum.  On the fast path it takes the logits two at
+            // a time (elements e - 1 and e, e odd) in a v_max3 written as asm,
+            // so it stays in this slot: as plain code the compiler sank the
+            // whole max chain below the phase's last MFMA, where nothing hides
+            // it.  (The general path keeps plain code: its address registers
+            // leave no room for the pinned operands.)
+            if constexpr (FAST) {
+                if (e & 1)
+                    asm volatile("v_max3_f32 %0, %0, %1, %2"
+                                 : "+v"(mxa)
+                                 : "v"(sn[(e - 1) >> 4][(e - 1) & 15]), "v"(sn[kb][i]));
+            } else {
+                mxa = fmaxf(mxa, v);
+            }
         };
 
         // phase B: the remaining PV MFMAs with the K(kt+3) copies, the first
@@ -836,6 +849,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
 #pragma unroll
                 for (int e = j * 32 / NB; e < (j + 1) * 32 / NB; ++e) post_el(e);
             }
+            // the row sum is a chain that only the step's end reads: pinned to
+            // its slot (fast path), or the compiler sinks the whole chain below
+            // the last MFMA, where nothing hides it
+            if constexpr (FAST) asm volatile("" : "+v"(psum));
             PA_FENCE();
         }
         l_run += psum;
