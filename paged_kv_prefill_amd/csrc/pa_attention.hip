@@ -684,6 +684,8 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
     // HAS_NEXT: tile kt+1 exists; MASK_NEXT: it needs masking
     // kin: the first PFQ K operands of tile kt+1, read by the previous step;
     // kout: the same for tile kt+2, read here in phase B
+    // phase B's row-sum and maximum chains pinned to their slots (see post_el)
+    constexpr bool PIN = FAST || C::K_I8;
     auto step = [&](int kt, int cur, f32x16 (&sc)[2], f32x16 (&sn)[2], u32x4 (&kin)[PFQ],
                     u32x4 (&kout)[PFQ], auto has_next, auto mask_next, auto v_ranged) PA_INL {
         constexpr bool NEXT = decltype(has_next)::value;
@@ -817,13 +819,15 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
             if constexpr (MASK)
                 if (tile_key(32 * kb + 8 * (i >> 2) + (i & 3), C::RPI) > lim) v = -INFINITY;
             sn[kb][i] = v;
-            // the running maximum.  On the fast path it takes the logits two at
-            // a time (elements e - 1 and e, e odd) in a v_max3 written as asm,
-            // so it stays in this slot: as plain code the compiler sank the
-            // whole max chain below the phase's last MFMA, where nothing hides
-            // it.  (The general path keeps plain code: its address registers
-            // leave no room for the pinned operands.)
-            if constexpr (FAST) {
+            // the running maximum.  On the fast bf16 path and the int8-KV K
+            // images it takes the logits two at a time (elements e - 1 and e,
+            // e odd) in a v_max3 written as asm, so it stays in this slot: as
+            // plain code the compiler sank the whole max chain below the
+            // phase's last MFMA, where nothing hides it.  (The general bf16
+            // path keeps plain code: its address registers leave no room for
+            // the pinned operands; the int8-QK arm's chain stays in its slots
+            // by itself.)
+            if constexpr (PIN) {
                 if (e & 1)
                     asm volatile("v_max3_f32 %0, %0, %1, %2"
                                  : "+v"(mxa)
@@ -850,9 +854,9 @@ __global__ __launch_bounds__(NTHR, 1) void attn_kernel(const AttnParams P) {
                 for (int e = j * 32 / NB; e < (j + 1) * 32 / NB; ++e) post_el(e);
             }
             // the row sum is a chain that only the step's end reads: pinned to
-            // its slot (fast path), or the compiler sinks the whole chain below
-            // the last MFMA, where nothing hides it
-            if constexpr (FAST) asm volatile("" : "+v"(psum));
+            // its slot (see the running maximum), or the compiler sinks the
+            // whole chain below the last MFMA, where nothing hides it
+            if constexpr (PIN) asm volatile("" : "+v"(psum));
             PA_FENCE();
         }
         l_run += psum;
