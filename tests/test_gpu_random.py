@@ -1,0 +1,104 @@
+"""Seeded random configurations through every attention entry point.
+
+24 small batches drawn from one seeded generator: 1-3 requests, contexts of
+1-700 tokens, chunks of 0-70 rows (at least one non-empty), block sizes from
+1 to 880 (on and off the 16-key multiple, so the fast and the general
+addressing paths), head_dim 64 / 128 / 256, 1-4 KV heads with 1-8 q heads
+each, causal or not.  Each batch runs the bf16 entry, the bf16 split-KV entry
+(1-7 splits), the int8 exact-QK entry, the int8-QK arm and both decode-shaped
+verify entries (1-9 splits), each against the oracle at its gate: 1e-3 for
+bf16 and verify (neither rounds V), 1e-3 plus the fp16 V-rounding bound for
+the int8 exact-QK arm, and the int8-QK arm against its exact emulation with
+the same bound; the K passes bit for bit.  Nothing in the draws is chosen for
+the kernels: it is a sweep for paths the named cases miss.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_prefill_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def gc():
+    import gpu_cases
+    return gpu_cases
+
+
+def draw_configs(n=24, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.integers(1, 4))
+        D = int(rng.choice([64, 128, 256]))
+        hkv = int(rng.choice([1, 2, 4]))
+        grp = int(rng.choice([1, 2, 3, 4, 8]))
+        bs = int(rng.choice([1, 3, 7, 16, 32, 48, 64, 880]))
+        causal = bool(rng.random() < 0.8)
+        ctx = [int(c) for c in rng.integers(1, 701, R)]
+        ql = [int(rng.integers(0, min(c, 70) + 1)) for c in ctx]
+        if max(ql) == 0:
+            ql[0] = min(ctx[0], 1 + int(rng.integers(0, 70)))
+        s_split = int(rng.integers(1, 8))
+        s_verify = int(rng.integers(1, 10))
+        out.append((500 + i, ql, ctx, bs, hkv * grp, hkv, D, causal, s_split, s_verify))
+    return out
+
+
+CONFIGS = draw_configs()
+IDS = [f"r{c[0]}" for c in CONFIGS]
+
+
+def rows_of(w):
+    return np.arange(int(w.q_lens.sum()), dtype=np.int32)
+
+
+@pytest.mark.parametrize("c", CONFIGS, ids=IDS)
+def test_random_config_all_entries(orc, c):
+    G = gc()
+    seed, ql, ctx, bs, hq, hkv, d, causal, s_split, s_verify = c
+    tag = f"{seed}: q {ql} ctx {ctx} bs {bs} Hq {hq} Hkv {hkv} D {d} causal {causal}"
+    print(tag, flush=True)
+    # bf16 KV: plain, split-KV, verify
+    w = synth.make_case(seed, ql, ctx, bs, hq, hkv, d, kv_format="bf16", causal=causal)
+    case = G.DevCase(w)
+    pools = synth.host_pools(w)
+    ref = G.oracle_rows(orc, w, pools, None)
+    e_plain, ok_plain = G.gate(case.run_bf16(), ref, ATOL)
+    out_s, _, _, _ = case.run_split(s_split)
+    e_split, ok_split = G.gate(out_s, ref, ATOL)
+    out_v, _, _, _ = case.run_verify(s_verify)
+    e_ver, ok_ver = G.gate(out_v, ref, ATOL)
+    del case
+    # int8 per-token-head KV (written by the library's writer): exact-QK,
+    # int8-QK with its K passes, verify
+    w8 = synth.make_case(seed, ql, ctx, bs, hq, hkv, d, kv_format="int8", causal=causal)
+    case8 = G.DevCase(w8)
+    wq = G.host_workload(w8, orc)
+    G.check_int8_pools(case8, wq)
+    p8 = synth.host_pools(wq)
+    ref8 = G.oracle_rows(orc, wq, p8, None)
+    vb = G.v_rounding_bound(orc, wq, p8)
+    e_i8, ok_i8 = G.gate(case8.run_int8kv(), ref8, ATOL, vb)
+    out_q, ks, k8 = case8.run_int8qk()
+    ks_ref = orc.k_stats(wq.block_table, wq.ctx_lens, p8["k"], p8["k_scales"])
+    k8_ref = orc.k_quant(wq.block_table, wq.ctx_lens, p8["k"], ks_ref, p8["k_scales"])
+    assert np.array_equal(ks.cpu().numpy().view(np.int32), ks_ref.view(np.int32))
+    assert np.array_equal(k8.cpu().numpy(), k8_ref)
+    emu = orc.prefill_int8qk(wq.block_table, wq.cu_q_lens, wq.ctx_lens, wq.q, k8_ref, ks_ref, p8["v"],
+                             wq.softmax_scale, causal=wq.causal, v_scales=p8["v_scales"])
+    e_q, ok_q = G.gate(out_q, emu, ATOL, vb)
+    out_v8, _, _, _ = case8.run_verify(s_verify, arm="int8")
+    e_v8, ok_v8 = G.gate(out_v8, ref8, ATOL)
+    print(f"   bf16 {e_plain:.2g}, split x{s_split} {e_split:.2g}, verify x{s_verify} {e_ver:.2g}; "
+          f"int8 exact {e_i8:.2g}, int8-QK {e_q:.2g}, verify {e_v8:.2g}", flush=True)
+    assert ok_plain and ok_split and ok_ver and ok_i8 and ok_q and ok_v8
