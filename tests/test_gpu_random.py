@@ -9,7 +9,8 @@ each, causal or not.  Each batch runs the bf16 entry, the bf16 split-KV entry
 verify entries (1-9 splits), each against the oracle at its gate: 1e-3 for
 bf16 and verify (neither rounds V), 1e-3 plus the fp16 V-rounding bound for
 the int8 exact-QK arm, and the int8-QK arm against its exact emulation with
-the same bound; the K passes bit for bit.  Nothing in the draws is chosen for
+the same bound; the K passes bit for bit; fp8 KV through the dense scratch
+(the scratch bit for bit) and read directly, at 1e-3.  Nothing in the draws is chosen for
 the kernels: it is a sweep for paths the named cases miss.
 """
 import numpy as np
@@ -99,6 +100,31 @@ def test_random_config_all_entries(orc, c):
     e_q, ok_q = G.gate(out_q, emu, ATOL, vb)
     out_v8, _, _, _ = case8.run_verify(s_verify, arm="int8")
     e_v8, ok_v8 = G.gate(out_v8, ref8, ATOL)
+    del case8
+    # fp8 e4m3 KV with per-tensor scales: the dense-scratch route and the direct read
+    wf = synth.make_case(seed, ql, ctx, bs, hq, hkv, d, kv_format="fp8", causal=causal)
+    casef = G.DevCase(wf)
+    pf = synth.host_pools(wf)
+    ref_direct = orc.prefill(wf.block_table, wf.cu_q_lens, wf.ctx_lens, wf.q, pf["k"], pf["v"],
+                             wf.softmax_scale, causal=wf.causal, k_scales=wf.k_scale,
+                             v_scales=wf.v_scale)
+    e_fd, ok_fd = G.gate(casef.run_fp8kv(), ref_direct, ATOL)
+    max_seq = int(wf.ctx_lens.max())
+    kref, vref = orc.fp8_dense_dequant(wf.block_table, wf.ctx_lens, pf["k"], pf["v"], wf.k_scale,
+                                       wf.v_scale, max_seq)
+    out_fs, ksc, vsc = casef.run_fp8(max_seq=max_seq)
+    for r in range(wf.num_reqs):
+        L = int(wf.ctx_lens[r])
+        assert np.array_equal(ksc.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[r, :L],
+                              kref[r, :L])
+        assert np.array_equal(vsc.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)[r, :L],
+                              vref[r, :L])
+    # the scratch route's reference: the oracle over the dequantised scratch,
+    # one block of max_seq tokens per request (identity block table)
+    ref_scratch = orc.prefill(np.arange(wf.num_reqs, dtype=np.int32)[:, None], wf.cu_q_lens,
+                              wf.ctx_lens, wf.q, kref, vref, wf.softmax_scale, causal=wf.causal)
+    e_fs, ok_fs = G.gate(out_fs, ref_scratch, ATOL)
     print(f"   bf16 {e_plain:.2g}, split x{s_split} {e_split:.2g}, verify x{s_verify} {e_ver:.2g}; "
-          f"int8 exact {e_i8:.2g}, int8-QK {e_q:.2g}, verify {e_v8:.2g}", flush=True)
-    assert ok_plain and ok_split and ok_ver and ok_i8 and ok_q and ok_v8
+          f"int8 exact {e_i8:.2g}, int8-QK {e_q:.2g}, verify {e_v8:.2g}; "
+          f"fp8 direct {e_fd:.2g}, scratch {e_fs:.2g}", flush=True)
+    assert ok_plain and ok_split and ok_ver and ok_i8 and ok_q and ok_v8 and ok_fd and ok_fs
