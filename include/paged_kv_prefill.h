@@ -47,7 +47,9 @@
  *     device lengths are inconsistent (Lq > L, L beyond what the block-table row
  *     can hold, L > max_ctx_len) are skipped and their outputs left untouched.
  *     A request with no chunk this call (Lq_r = 0) has no output rows; the
- *     other requests of the batch are computed as usual.
+ *     other requests of the batch are computed as usual.  A batch with
+ *     max_q_len = 0 has none at all: the call returns PA_OK and writes no
+ *     output (an attention entry point still builds its tile images).
  *   - Block ids outside [0, num_blocks) are a caller error: the kernels never
  *     touch memory outside the pool for them (they read zeros or a row of
  *     block 0 instead) and the outputs that depend on them are unspecified.

@@ -866,7 +866,7 @@ hipError_t launch_verify_merge(const VerifyParams &p, int head_dim, hipStream_t 
 }
 
 hipError_t launch_verify(bool int8, int head_dim, const VerifyParams &p, hipStream_t stream) {
-    if (p.splits < 1 || p.ctiles < 1) return hipErrorInvalidValue;
+    if (p.splits < 1 || p.ctiles < 0) return hipErrorInvalidValue;
     const int64_t nwg = (int64_t)p.num_reqs * p.Hkv * p.ctiles * p.splits;
     if (nwg <= 0) return hipSuccess;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;

@@ -183,6 +183,46 @@ def test_int8qk_zero_query_rows(orc):
     assert ok
 
 
+EMPTY_ARMS = ["bf16", "bf16_split", "int8kv", "int8kv_split", "int8qk", "fp8kv", "verify_bf16",
+              "verify_bf16_split", "verify_int8kv", "verify_int8kv_split"]
+
+
+@pytest.mark.parametrize("arm", EMPTY_ARMS)
+def test_empty_batch_writes_nothing(arm):
+    """A batch with no chunk rows at all (every Lq_r = 0, max_q_len = 0): each
+    attention entry point returns without error and leaves every output and
+    partial buffer as it was (NaN-filled here), the split and verify merges
+    included."""
+    G = gc()
+    from paged_kv_prefill_amd import ops
+    fmt = "bf16" if "bf16" in arm else ("fp8" if arm == "fp8kv" else "int8")
+    w = synth.make_case(171, [5, 9], [40, 300], 16, 8, 2, 128, kv_format=fmt)
+    case = G.DevCase(w)
+    case.cu_q = G.dev(np.zeros(w.num_reqs + 1, np.int32))
+    plain = case.paged
+
+    def empty_paged(which=0, causal=None):
+        p = plain(which, causal)
+        p.max_q_len = 0
+        return p
+
+    case.paged = empty_paged
+    print(f"empty batch: {arm}", flush=True)
+    if arm in ("bf16", "int8kv", "fp8kv"):
+        bufs = [getattr(case, "run_" + arm)()]
+    elif arm == "int8qk":
+        bufs = [case.run_int8qk()[0]]
+    elif arm.startswith("verify"):
+        a = arm.split("_")[1]
+        bufs = case.run_verify(4 if arm.endswith("split") else 1, arm=a)
+    else:
+        bufs = case.run_split(4, arm=arm.split("_")[0])
+    torch.cuda.synchronize()
+    for b in bufs:
+        if b is not None:
+            assert torch.isnan(b).all().item(), f"{arm}: an output was written"
+
+
 @pytest.mark.parametrize("c", SMALL, ids=IDS)
 def test_small_fp8_dense(orc, c):
     G = gc()
