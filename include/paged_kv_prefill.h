@@ -50,6 +50,8 @@
  *     other requests of the batch are computed as usual.  A batch with
  *     max_q_len = 0 has none at all: the call returns PA_OK and writes no
  *     output (an attention entry point still builds its tile images).
+ *   - At most 65,535 requests and 65,535 KV heads per call (launch-grid
+ *     axes); more return PA_ERR_TOO_LARGE.
  *   - Block ids outside [0, num_blocks) are a caller error: the kernels never
  *     touch memory outside the pool for them (they read zeros or a row of
  *     block 0 instead) and the outputs that depend on them are unspecified.

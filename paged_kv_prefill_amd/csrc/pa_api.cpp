@@ -47,6 +47,8 @@ int check_common(const pa_paged_args *a, int elem_bytes, bool needs_q) {
     if (a->stride_block % q16 || a->stride_tok % q16 || a->stride_head % q16) return PA_ERR_SHAPE;
     // a request's chunk-position arithmetic is int32 (positions < 2^31)
     if ((int64_t)a->max_ctx_len * a->num_kv_heads >= ((int64_t)1 << 31)) return PA_ERR_TOO_LARGE;
+    // requests and KV heads index launch-grid axes limited to 65,535
+    if (a->num_reqs > 65535 || a->num_kv_heads > 65535) return PA_ERR_TOO_LARGE;
     return PA_OK;
 }
 

@@ -69,6 +69,9 @@ BAD = [
     (dict(stride_tok=130), ops.PA_ERR_SHAPE),
     (dict(max_ctx_len=2 ** 30, max_q_len=8), ops.PA_ERR_TOO_LARGE),
     (dict(flags=4), ops.PA_ERR_SHAPE),
+    (dict(num_reqs=65536, stride_bt=1), ops.PA_ERR_TOO_LARGE),
+    (dict(num_q_heads=65536, num_kv_heads=65536, max_ctx_len=8, stride_block=4 * 65536 * 64,
+          stride_tok=65536 * 64), ops.PA_ERR_TOO_LARGE),
 ]
 
 
@@ -238,6 +241,23 @@ def test_store_argument_errors():
     assert L.pa_store_kv_fp8(C.byref(a), p, p, None, p, p, p, None) == ops.PA_ERR_NULL
     assert L.pa_store_kv_fp8(C.byref(a), p, p, p, p, odd, p, None) == ops.PA_ERR_SHAPE
     assert L.pa_store_kv_fp8(C.byref(_args(num_q_heads=3)), p, p, p, p, p, p, None) == ops.PA_ERR_SHAPE
+
+
+def test_request_and_head_limits_hold_for_every_entry():
+    """Requests and KV heads index launch-grid axes of every kernel: above
+    65,535 each entry point refuses the call before any HIP call."""
+    L = ops.lib()
+    p = C.c_void_p(4096)
+    many = C.byref(_args(num_reqs=65536, stride_bt=1))
+    big = 1 << 40
+    T = ops.PA_ERR_TOO_LARGE
+    assert L.pa_prefill_int8kv(many, p, p, p, p, p, p, 0, p, big, None) == T
+    assert L.pa_prefill_fp8kv(many, p, p, p, p, p, p, 0, p, big, None) == T
+    assert L.pa_k_stats(many, p, ops.PA_DTYPE_INT8, p, p, p, None) == T
+    assert L.pa_k_quant(many, p, ops.PA_DTYPE_INT8, p, p, p, p, None) == T
+    assert L.pa_store_kv_int8(many, p, p, p, p, p, p, None) == T
+    assert L.pa_fp8_dense_dequant(many, p, p, p, p, 16, p, p, None) == T
+    assert L.pa_verify_bf16(many, p, p, p, 1, None, None, p, 0, None, None) == T
 
 
 def _split_tiles(s, splits, t_full, n_tiles):
