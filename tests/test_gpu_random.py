@@ -11,8 +11,12 @@ bf16 and verify (neither rounds V), 1e-3 plus the fp16 V-rounding bound for
 the int8 exact-QK arm, and the int8-QK arm against its exact emulation with
 the same bound; the K passes bit for bit; fp8 KV through the dense scratch
 (the scratch bit for bit) and read directly, at 1e-3.  Nothing in the draws is chosen for
-the kernels: it is a sweep for paths the named cases miss.
+the kernels: it is a sweep for paths the named cases miss.  PA_RANDOM_N and
+PA_RANDOM_SEED in the environment widen the sweep (more batches, another
+generator seed) for a longer run.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -55,7 +59,8 @@ def draw_configs(n=24, seed=20261203):
     return out
 
 
-CONFIGS = draw_configs()
+CONFIGS = draw_configs(int(os.environ.get("PA_RANDOM_N", "24")),
+                       int(os.environ.get("PA_RANDOM_SEED", "20261203")))
 IDS = [f"r{c[0]}" for c in CONFIGS]
 
 
