@@ -11,9 +11,11 @@ bf16 and verify (neither rounds V), 1e-3 plus the fp16 V-rounding bound for
 the int8 exact-QK arm, and the int8-QK arm against its exact emulation with
 the same bound; the K passes bit for bit; fp8 KV through the dense scratch
 (the scratch bit for bit) and read directly, at 1e-3.  Nothing in the draws is chosen for
-the kernels: it is a sweep for paths the named cases miss.  PA_RANDOM_N and
-PA_RANDOM_SEED in the environment widen the sweep (more batches, another
-generator seed) for a longer run.
+the kernels: it is a sweep for paths the named cases miss.  Six larger batches
+(contexts up to 4,000 tokens, chunks up to 300 rows, up to 16 split-KV and 64
+verify splits) run the same checks over many tiles per workgroup.
+PA_RANDOM_N, PA_RANDOM_MEDIUM_N and PA_RANDOM_SEED in the environment widen
+the sweep (more batches, another generator seed) for a longer run.
 """
 import os
 
@@ -68,8 +70,43 @@ def rows_of(w):
     return np.arange(int(w.q_lens.sum()), dtype=np.int32)
 
 
+def draw_medium_configs(n=6, seed=20261204):
+    """Fewer, larger batches: 1-4 requests, contexts up to 4,000 tokens (tens of
+    64-key tiles, so many workgroups per request, the work schedule and long
+    key loops), chunks up to 300 rows, up to 16 split-KV and 64 verify splits."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.integers(1, 5))
+        D = int(rng.choice([64, 128, 256]))
+        hkv = int(rng.choice([1, 2, 4]))
+        grp = int(rng.choice([1, 2, 4, 8]))
+        bs = int(rng.choice([1, 7, 16, 48, 64, 880]))
+        causal = bool(rng.random() < 0.8)
+        ctx = [int(c) for c in rng.integers(1, 4001, R)]
+        ql = [int(rng.integers(0, min(c, 300) + 1)) for c in ctx]
+        if max(ql) == 0:
+            ql[0] = min(ctx[0], 1 + int(rng.integers(0, 300)))
+        out.append((900 + i, ql, ctx, bs, hkv * grp, hkv, D, causal, int(rng.integers(1, 17)),
+                    int(rng.integers(1, 65))))
+    return out
+
+
+MEDIUM = draw_medium_configs(int(os.environ.get("PA_RANDOM_MEDIUM_N", "6")),
+                             int(os.environ.get("PA_RANDOM_SEED", "20261203")) + 1)
+
+
 @pytest.mark.parametrize("c", CONFIGS, ids=IDS)
 def test_random_config_all_entries(orc, c):
+    check_all_entries(orc, c)
+
+
+@pytest.mark.parametrize("c", MEDIUM, ids=[f"m{c[0]}" for c in MEDIUM])
+def test_random_medium_config_all_entries(orc, c):
+    check_all_entries(orc, c)
+
+
+def check_all_entries(orc, c):
     G = gc()
     seed, ql, ctx, bs, hq, hkv, d, causal, s_split, s_verify = c
     tag = f"{seed}: q {ql} ctx {ctx} bs {bs} Hq {hq} Hkv {hkv} D {d} causal {causal}"
