@@ -10,7 +10,11 @@ verify entries (1-9 splits), each against the oracle at its gate: 1e-3 for
 bf16 and verify (neither rounds V), 1e-3 plus the fp16 V-rounding bound for
 the int8 exact-QK arm, and the int8-QK arm against its exact emulation with
 the same bound; the K passes bit for bit; fp8 KV through the dense scratch
-(the scratch bit for bit) and read directly, at 1e-3.  Nothing in the draws is chosen for
+(the scratch bit for bit) and read directly, at 1e-3.  On the bf16, int8 exact-QK and
+fp8 entries the workspace flags must reproduce the plain call bit for bit:
+PA_FLAG_APPEND after a call over the contexts without their chunks (so the
+tiles the chunk touches have to be rebuilt), then PA_FLAG_IMAGES_READY.
+Nothing in the draws is chosen for
 the kernels: it is a sweep for paths the named cases miss.  Six larger batches
 (contexts up to 4,000 tokens, chunks up to 300 rows, up to 16 split-KV and 64
 verify splits) run the same checks over many tiles per workgroup.
@@ -39,6 +43,11 @@ def _need_gpu():
 def gc():
     import gpu_cases
     return gpu_cases
+
+
+def ops():
+    from paged_kv_prefill_amd import ops as o
+    return o
 
 
 def draw_configs(n=24, seed=20261203):
@@ -106,6 +115,31 @@ def test_random_medium_config_all_entries(orc, c):
     check_all_entries(orc, c)
 
 
+def check_workspace_paths(case, entry, run, ref_out):
+    """The workspace flags on one entry point, against its plain call's output
+    ref_out, bit for bit: a call that finds the images in place
+    (PA_FLAG_IMAGES_READY), and an incremental call (PA_FLAG_APPEND) after one
+    that built the images of the contexts before this chunk (every context
+    shorter by its chunk, no chunk rows) on the same workspace, so that the
+    tiles the chunk touches must be rebuilt for the result to hold."""
+    from paged_kv_prefill_amd import ops
+    w = case.w
+    ws = ops.workspace(case.paged(), entry)
+    before = ops.Paged(case.bts[0], gc().dev(np.zeros(w.num_reqs + 1, np.int32)),
+                       gc().dev((w.ctx_lens - w.q_lens).astype(np.int32)), 0, int(w.ctx_lens.max()),
+                       w.block_size, w.num_blocks, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                       w.softmax_scale, w.causal)
+    unused = case.out()
+    run(before, unused, ws)
+    assert torch.isnan(unused).all().item(), "a call without chunk rows wrote output"
+    for flag in (ops.PA_FLAG_APPEND, ops.PA_FLAG_IMAGES_READY):
+        p = case.paged()
+        p.flags = flag
+        o = case.out()
+        run(p, o, ws)
+        assert torch.equal(o, ref_out), f"flag {flag}: output differs from the plain call"
+
+
 def check_all_entries(orc, c):
     G = gc()
     seed, ql, ctx, bs, hq, hkv, d, causal, s_split, s_verify = c
@@ -116,7 +150,11 @@ def check_all_entries(orc, c):
     case = G.DevCase(w)
     pools = synth.host_pools(w)
     ref = G.oracle_rows(orc, w, pools, None)
-    e_plain, ok_plain = G.gate(case.run_bf16(), ref, ATOL)
+    out_plain = case.run_bf16()
+    e_plain, ok_plain = G.gate(out_plain, ref, ATOL)
+    check_workspace_paths(case, ops().PA_ENTRY_PREFILL_BF16,
+                          lambda p, o, ws: ops().pa_prefill_bf16(p, case.q, case.k_pool, case.v_pool, o, ws),
+                          out_plain)
     out_s, _, _, _ = case.run_split(s_split)
     e_split, ok_split = G.gate(out_s, ref, ATOL)
     out_v, _, _, _ = case.run_verify(s_verify)
@@ -131,7 +169,12 @@ def check_all_entries(orc, c):
     p8 = synth.host_pools(wq)
     ref8 = G.oracle_rows(orc, wq, p8, None)
     vb = G.v_rounding_bound(orc, wq, p8)
-    e_i8, ok_i8 = G.gate(case8.run_int8kv(), ref8, ATOL, vb)
+    out_i8 = case8.run_int8kv()
+    e_i8, ok_i8 = G.gate(out_i8, ref8, ATOL, vb)
+    check_workspace_paths(case8, ops().PA_ENTRY_PREFILL_INT8KV,
+                          lambda p, o, ws: ops().pa_prefill_int8kv(p, case8.q, case8.k_pool, case8.v_pool,
+                                                                   case8.k_scales, case8.v_scales, o, ws),
+                          out_i8)
     out_q, ks, k8 = case8.run_int8qk()
     ks_ref = orc.k_stats(wq.block_table, wq.ctx_lens, p8["k"], p8["k_scales"])
     k8_ref = orc.k_quant(wq.block_table, wq.ctx_lens, p8["k"], ks_ref, p8["k_scales"])
@@ -150,7 +193,12 @@ def check_all_entries(orc, c):
     ref_direct = orc.prefill(wf.block_table, wf.cu_q_lens, wf.ctx_lens, wf.q, pf["k"], pf["v"],
                              wf.softmax_scale, causal=wf.causal, k_scales=wf.k_scale,
                              v_scales=wf.v_scale)
-    e_fd, ok_fd = G.gate(casef.run_fp8kv(), ref_direct, ATOL)
+    out_fd = casef.run_fp8kv()
+    e_fd, ok_fd = G.gate(out_fd, ref_direct, ATOL)
+    check_workspace_paths(casef, ops().PA_ENTRY_PREFILL_FP8KV,
+                          lambda p, o, ws: ops().pa_prefill_fp8kv(p, casef.q, casef.k_pool, casef.v_pool,
+                                                                  casef.k_scale, casef.v_scale, o, ws),
+                          out_fd)
     max_seq = int(wf.ctx_lens.max())
     kref, vref = orc.fp8_dense_dequant(wf.block_table, wf.ctx_lens, pf["k"], pf["v"], wf.k_scale,
                                        wf.v_scale, max_seq)
