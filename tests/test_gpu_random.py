@@ -10,10 +10,11 @@ verify entries (1-9 splits), each against the oracle at its gate: 1e-3 for
 bf16 and verify (neither rounds V), 1e-3 plus the fp16 V-rounding bound for
 the int8 exact-QK arm, and the int8-QK arm against its exact emulation with
 the same bound; the K passes bit for bit; fp8 KV through the dense scratch
-(the scratch bit for bit) and read directly, at 1e-3.  On the bf16, int8 exact-QK and
-fp8 entries the workspace flags must reproduce the plain call bit for bit:
-PA_FLAG_APPEND after a call over the contexts without their chunks (so the
-tiles the chunk touches have to be rebuilt), then PA_FLAG_IMAGES_READY.
+(the scratch bit for bit) and read directly, at 1e-3.  On the bf16, int8 exact-QK,
+int8-QK and fp8 entries the workspace flags must reproduce the plain call bit
+for bit: PA_FLAG_APPEND after a call over the contexts without their chunks
+(so the tiles the chunk touches have to be rebuilt), then
+PA_FLAG_IMAGES_READY; so must the allocation-free bf16 entry.
 Nothing in the draws is chosen for
 the kernels: it is a sweep for paths the named cases miss.  Six larger batches
 (contexts up to 4,000 tokens, chunks up to 300 rows, up to 16 split-KV and 64
@@ -155,6 +156,11 @@ def check_all_entries(orc, c):
     check_workspace_paths(case, ops().PA_ENTRY_PREFILL_BF16,
                           lambda p, o, ws: ops().pa_prefill_bf16(p, case.q, case.k_pool, case.v_pool, o, ws),
                           out_plain)
+    # the allocation-free variant of the same call (the library's own array)
+    if ops().pa_workspace_bytes(case.paged(), ops().PA_ENTRY_PREFILL_BF16) <= ops().PA_NOALLOC_SCRATCH_BYTES:
+        out_na = case.out()
+        ops().pa_prefill_bf16_noalloc(case.paged(), case.q, case.k_pool, case.v_pool, out_na)
+        assert torch.equal(out_na, out_plain), "allocation-free call differs from the plain call"
     out_s, _, _, _ = case.run_split(s_split)
     e_split, ok_split = G.gate(out_s, ref, ATOL)
     out_v, _, _, _ = case.run_verify(s_verify)
@@ -183,6 +189,10 @@ def check_all_entries(orc, c):
     emu = orc.prefill_int8qk(wq.block_table, wq.cu_q_lens, wq.ctx_lens, wq.q, k8_ref, ks_ref, p8["v"],
                              wq.softmax_scale, causal=wq.causal, v_scales=p8["v_scales"])
     e_q, ok_q = G.gate(out_q, emu, ATOL, vb)
+    check_workspace_paths(case8, ops().PA_ENTRY_PREFILL_INT8QK,
+                          lambda p, o, ws: ops().pa_prefill_int8qk(p, case8.q, k8, ks, case8.cu_ctx,
+                                                                   case8.v_pool, case8.v_scales, o, ws),
+                          out_q)
     out_v8, _, _, _ = case8.run_verify(s_verify, arm="int8")
     e_v8, ok_v8 = G.gate(out_v8, ref8, ATOL)
     del case8
