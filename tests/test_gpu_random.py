@@ -4,11 +4,12 @@
 1-700 tokens, chunks of 0-70 rows (at least one non-empty), block sizes from
 1 to 880 (on and off the 16-key multiple, so the fast and the general
 addressing paths), head_dim 64 / 128 / 256, 1-4 KV heads with 1-8 q heads
-each, causal or not.  Each batch runs the bf16 entry, the bf16 split-KV entry
+each, causal or not.  Each batch runs the bf16 entry, both split-KV entries
 (1-7 splits), the int8 exact-QK entry, the int8-QK arm and both decode-shaped
 verify entries (1-9 splits), each against the oracle at its gate: 1e-3 for
 bf16 and verify (neither rounds V), 1e-3 plus the fp16 V-rounding bound for
-the int8 exact-QK arm, and the int8-QK arm against its exact emulation with
+the int8 exact-QK arm and its split entry, the split and verify log-sum-exp
+within 1e-4, and the int8-QK arm against its exact emulation with
 the same bound; the K passes bit for bit; fp8 KV through the dense scratch
 (the scratch bit for bit) and read directly, at 1e-3.  On the bf16, int8 exact-QK,
 int8-QK and fp8 entries the workspace flags must reproduce the plain call bit
@@ -33,6 +34,7 @@ from paged_kv_prefill_amd import synth
 pytestmark = pytest.mark.gpu
 
 ATOL = 1e-3
+LSE_ATOL = 1e-4   # the split-KV and verify log-sum-exp, natural log
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -74,6 +76,19 @@ def draw_configs(n=24, seed=20261203):
 CONFIGS = draw_configs(int(os.environ.get("PA_RANDOM_N", "24")),
                        int(os.environ.get("PA_RANDOM_SEED", "20261203")))
 IDS = [f"r{c[0]}" for c in CONFIGS]
+
+
+def lse_ref(orc, w, pools):
+    """The oracle's output and natural-log log-sum-exp of every chunk row."""
+    return orc.prefill_lse(w.block_table, w.cu_q_lens, w.ctx_lens, w.q, pools["k"], pools["v"],
+                           w.softmax_scale, causal=w.causal, k_scales=pools.get("k_scales"),
+                           v_scales=pools.get("v_scales"))
+
+
+def lse_err(lse, ref_lse):
+    got = lse.double().cpu().numpy()
+    assert np.all(np.isfinite(got)), "non-finite log-sum-exp"
+    return float(np.max(np.abs(got - ref_lse))) if got.size else 0.0
 
 
 def rows_of(w):
@@ -150,7 +165,7 @@ def check_all_entries(orc, c):
     w = synth.make_case(seed, ql, ctx, bs, hq, hkv, d, kv_format="bf16", causal=causal)
     case = G.DevCase(w)
     pools = synth.host_pools(w)
-    ref = G.oracle_rows(orc, w, pools, None)
+    ref, ref_lse = lse_ref(orc, w, pools)
     out_plain = case.run_bf16()
     e_plain, ok_plain = G.gate(out_plain, ref, ATOL)
     check_workspace_paths(case, ops().PA_ENTRY_PREFILL_BF16,
@@ -161,10 +176,11 @@ def check_all_entries(orc, c):
         out_na = case.out()
         ops().pa_prefill_bf16_noalloc(case.paged(), case.q, case.k_pool, case.v_pool, out_na)
         assert torch.equal(out_na, out_plain), "allocation-free call differs from the plain call"
-    out_s, _, _, _ = case.run_split(s_split)
+    out_s, lse_s, _, _ = case.run_split(s_split)
     e_split, ok_split = G.gate(out_s, ref, ATOL)
-    out_v, _, _, _ = case.run_verify(s_verify)
+    out_v, lse_v, _, _ = case.run_verify(s_verify)
     e_ver, ok_ver = G.gate(out_v, ref, ATOL)
+    l_err = max(lse_err(lse_s, ref_lse), lse_err(lse_v, ref_lse))
     del case
     # int8 per-token-head KV (written by the library's writer): exact-QK,
     # int8-QK with its K passes, verify
@@ -173,8 +189,10 @@ def check_all_entries(orc, c):
     wq = G.host_workload(w8, orc)
     G.check_int8_pools(case8, wq)
     p8 = synth.host_pools(wq)
-    ref8 = G.oracle_rows(orc, wq, p8, None)
+    ref8, ref8_lse = lse_ref(orc, wq, p8)
     vb = G.v_rounding_bound(orc, wq, p8)
+    out_s8, lse_s8, _, _ = case8.run_split(s_split, arm="int8")
+    e_s8, ok_s8 = G.gate(out_s8, ref8, ATOL, vb)
     out_i8 = case8.run_int8kv()
     e_i8, ok_i8 = G.gate(out_i8, ref8, ATOL, vb)
     check_workspace_paths(case8, ops().PA_ENTRY_PREFILL_INT8KV,
@@ -193,8 +211,9 @@ def check_all_entries(orc, c):
                           lambda p, o, ws: ops().pa_prefill_int8qk(p, case8.q, k8, ks, case8.cu_ctx,
                                                                    case8.v_pool, case8.v_scales, o, ws),
                           out_q)
-    out_v8, _, _, _ = case8.run_verify(s_verify, arm="int8")
+    out_v8, lse_v8, _, _ = case8.run_verify(s_verify, arm="int8")
     e_v8, ok_v8 = G.gate(out_v8, ref8, ATOL)
+    l_err = max(l_err, lse_err(lse_s8, ref8_lse), lse_err(lse_v8, ref8_lse))
     del case8
     # fp8 e4m3 KV with per-tensor scales: the dense-scratch route and the direct read
     wf = synth.make_case(seed, ql, ctx, bs, hq, hkv, d, kv_format="fp8", causal=causal)
@@ -225,6 +244,7 @@ def check_all_entries(orc, c):
                               wf.ctx_lens, wf.q, kref, vref, wf.softmax_scale, causal=wf.causal)
     e_fs, ok_fs = G.gate(out_fs, ref_scratch, ATOL)
     print(f"   bf16 {e_plain:.2g}, split x{s_split} {e_split:.2g}, verify x{s_verify} {e_ver:.2g}; "
-          f"int8 exact {e_i8:.2g}, int8-QK {e_q:.2g}, verify {e_v8:.2g}; "
-          f"fp8 direct {e_fd:.2g}, scratch {e_fs:.2g}", flush=True)
-    assert ok_plain and ok_split and ok_ver and ok_i8 and ok_q and ok_v8 and ok_fd and ok_fs
+          f"int8 exact {e_i8:.2g}, split {e_s8:.2g}, int8-QK {e_q:.2g}, verify {e_v8:.2g}; "
+          f"fp8 direct {e_fd:.2g}, scratch {e_fs:.2g}; lse {l_err:.2g}", flush=True)
+    assert ok_plain and ok_split and ok_ver and ok_i8 and ok_s8 and ok_q and ok_v8 and ok_fd and ok_fs
+    assert l_err <= LSE_ATOL
