@@ -110,6 +110,30 @@ def test_split_matches_oracle(orc, c, splits):
     assert np.array_equal(bits(lse16), bits(lse))
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "int8"])
+def test_more_splits_than_one_merge_batch(orc, fmt):
+    """Split counts beyond the merge's 64-split batch, up to PA_MAX_SPLITS: a
+    9,000-token context whose 64-row chunk leaves 139 unmasked tiles, so 100
+    splits all take keys and 256 splits leave 117 empty (-inf) ones, and the
+    merge walks its later batches over both kinds."""
+    G = gc()
+    w = synth.make_case(210, [64], [9000], 16, 8, 2, 128, kv_format=fmt)
+    case = G.DevCase(w)
+    wq = G.host_workload(w, orc)
+    pools = synth.host_pools(wq)
+    if fmt == "int8":
+        G.check_int8_pools(case, wq)
+    ref, ref_lse = oracle_lse(orc, wq, pools)
+    vb = G.v_rounding_bound(orc, wq, pools) if fmt == "int8" else None
+    arm = "bf16" if fmt == "bf16" else "int8kv"
+    for splits in (100, 256):
+        out, lse, _, _ = case.run_split(splits, arm=arm)
+        err, ok = G.gate(out, ref, ATOL, vb)
+        lerr = float(np.max(np.abs(np64(lse) - ref_lse)))
+        print(f"{fmt} splits {splits}: out err {err:.3g}, lse err {lerr:.3g}", flush=True)
+        assert ok and lerr <= LSE_ATOL
+
+
 @pytest.mark.parametrize("c", [CASES[2], CASES[3], CASES[4]], ids=["s203", "s204", "s205"])
 def test_split_partials_match_oracle_ranges(orc, c):
     """Each split's partial O and log-sum-exp are the oracle's attention over
