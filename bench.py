@@ -20,7 +20,7 @@ launch time, against the bf16 dense MFMA peak, and also against the MFMA
 throughput the chip sustains on the same instruction shape with no other work
 (pa_peak_probe, measured in the same run); timed with the image pass
 skipped via PA_FLAG_IMAGES_READY), its HBM bytes per launch from the committed
-counter profile when that was taken on this build, the CPU oracle's rate over
+counter profile when that profile names the loaded library's build id, the CPU oracle's rate over
 the same 2,048-row chunk, and the other arms (the headline with a bf16 output, int8 KV
 exact-QK, int8-QK with its fused K pass (and the two separate passes), fp8 KV through the dense
 bf16 scratch, the batched 8-request chunk,
@@ -672,7 +672,7 @@ def main():
     WARM_S = max(0.0, args.warm_seconds)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
